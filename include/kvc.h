@@ -1,0 +1,171 @@
+/*
+ * kvc.h - paged KV-cache append, paged GQA decode attention and chunked-prefill
+ * attention for AMD MI355X (gfx950). C ABI: plain pointers and sizes only.
+ *
+ * What the library computes (restated from the pages it follows):
+ *   - A decode step computes one new position's query, key and value, appends
+ *     the key and value to the cache and attends the new query over everything
+ *     stored (aiwithghost.com "KV cache and continuous batching: 1,000 people ask
+ *     AI", section "What does a KV cache keep?"; daviddominguez.dev "The KV cache
+ *     and prefix caching", section "What prefill stores and decode reads").
+ *   - The cache is held in fixed-size blocks reached through a per-sequence block
+ *     table, not in one contiguous slab per request (daviddominguez.dev, same
+ *     section, on the PagedAttention design); blocks hold 16 tokens
+ *     (daviddominguez.dev, section "A prefix already in the cache can skip its
+ *     prefill").
+ *   - Several query heads share one key/value head (grouped-query attention,
+ *     daviddominguez.dev, section "What prefill stores and decode reads").
+ *   - Prefill runs in chunks of a fixed token budget (gouthm.com "The KV cache is
+ *     not your bottleneck", section "The fix that mattered") and can start after
+ *     a cached prefix (daviddominguez.dev, section "A prefix already in the cache
+ *     can skip its prefill").
+ *
+ * Attention of query head h at position t:
+ *     s_j = scale * <q_t[h], k_j[h / G]>,  j = 0..t (the token sees itself)
+ *     o   = sum_j softmax(s)_j * v_j[h / G],   G = Hq / Hkv
+ * arithmetic in fp32, inputs and outputs in the cache dtype.
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or synchronises; it keeps no state between calls
+ *     and is safe to call from several host threads.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *     enqueues work on it and returns.
+ *   - Host-side validation happens before any launch: on a negative status
+ *     nothing was enqueued. Device-side contract violations (a block id outside
+ *     [0, num_blocks), a slot outside the pool, a context longer than the block
+ *     table) never touch memory out of bounds: the offending read or write is
+ *     skipped (reads yield zero) and, if `err_flag` is non-NULL, a bit is OR-ed
+ *     into that device int32 (KVC_DEVERR_*).
+ *   - Cache layout, per layer and per K / V:
+ *         [num_blocks][num_kv_heads][block_size = 16][head_dim]
+ *     so one (block, kv-head) tile is contiguous (4 KiB for head_dim 128, bf16).
+ *   - Supported: dtype fp32 (head_dim 16, 32, 64, 128) and bf16 (head_dim 32,
+ *     64, 128); G = Hq / Hkv in {1, 2, 4, 8}; block_size 16.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+enum {
+  KVC_OK = 0,
+  KVC_ERR_NULL = -1,        /* a required pointer is NULL */
+  KVC_ERR_SHAPE = -2,       /* inconsistent sizes (Hq % Hkv, negative counts, ...) */
+  KVC_ERR_DTYPE = -3,       /* unknown dtype */
+  KVC_ERR_UNSUPPORTED = -4, /* head_dim / block_size / G outside the supported set */
+  KVC_ERR_WORKSPACE = -5,   /* workspace missing or smaller than the size query */
+  KVC_ERR_LAUNCH = -6       /* the HIP runtime rejected a launch */
+};
+
+/* Bits OR-ed into cache->err_flag by kernels that skipped an invalid access. */
+enum {
+  KVC_DEVERR_BLOCK_ID = 1,  /* block table entry outside [0, num_blocks) */
+  KVC_DEVERR_SLOT = 2,      /* slot outside [0, num_blocks * block_size) */
+  KVC_DEVERR_CONTEXT = 4    /* context needs more blocks than the table row has */
+};
+
+/* One layer's paged cache. Pointers are device memory owned by the caller. */
+typedef struct {
+  void* k_cache;      /* [num_blocks][num_kv_heads][block_size][head_dim], dtype */
+  void* v_cache;      /* same shape */
+  int32_t num_blocks;
+  int32_t block_size; /* must be 16 */
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;      /* kvc_dtype */
+  int32_t* err_flag;  /* optional device int32 (may be NULL), see KVC_DEVERR_* */
+} kvc_cache;
+
+/* Host-only. Raw K+V bytes one token occupies across `layers` layers:
+ * 2 * layers * kv_heads * head_dim * dtype_bytes (aiwithghost.com, section "How
+ * KV cache memory limits concurrency"; daviddominguez.dev, section "What prefill
+ * stores and decode reads"). Returns -1 on a negative argument. */
+int64_t kvc_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
+                               int32_t dtype_bytes);
+
+/* Slot of each new token: slot[t] = block_table[seq_ids[t]][p / bs] * bs + p % bs
+ * with p = positions[t]; p < 0 gives slot -1 (a padding token).
+ *   block_table  device int32 [n_seqs][max_blocks] (row-major)
+ *   seq_ids      device int32 [T], row of block_table for each token; a row
+ *                outside [0, n_seqs) gives slot -1 and KVC_DEVERR_CONTEXT
+ *   positions    device int32 [T], logical position of each token
+ *   slot_mapping device int64 [T], written
+ *   num_blocks   pool size, for the range check (bad ids give slot -1 + flag)
+ *   err_flag     optional device int32
+ * Block tables hold physical block ids in any order; the same ids are used by
+ * every layer's pool. */
+int kvc_slot_mapping(const int32_t* block_table, int32_t n_seqs, int32_t max_blocks,
+                     int32_t num_blocks, const int32_t* seq_ids, const int32_t* positions, int32_t T,
+                     int32_t block_size, int64_t* slot_mapping, int32_t* err_flag,
+                     void* stream);
+
+/* Append: k_cache[slot / bs][h][slot % bs][:] = k[t][h][:], same for v.
+ *   k, v          device [T][num_kv_heads][head_dim], cache dtype (no conversion:
+ *                 the cache contents are bit-exact copies)
+ *   slot_mapping  device int64 [T]; slot < 0 skips the token
+ * T may be 0 (nothing is launched). */
+int kvc_kv_append(const kvc_cache* cache, const int64_t* slot_mapping, const void* k,
+                  const void* v, int32_t T, void* stream);
+
+/* Bytes of scratch kvc_paged_decode_attention needs for these sizes (split-K
+ * partial results). Depends only on its arguments. */
+size_t kvc_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim,
+                                  int32_t max_context_len);
+
+/* Paged GQA decode attention for a batch of sequences of mixed lengths.
+ *   q             device [B][Hq][head_dim], cache dtype: each sequence's newest query
+ *   block_table   device int32 [B][max_blocks]
+ *   context_lens  device int32 [B]: tokens in each sequence's cache INCLUDING the
+ *                 newest one (append first, then attend). 0 gives a zero output.
+ *   max_context_len  host-known upper bound of context_lens (sizes the grid;
+ *                 no device-to-host copy is made)
+ *   softmax_scale usually 1/sqrt(head_dim)
+ *   out           device [B][Hq][head_dim], cache dtype (bf16 outputs are rounded
+ *                 to nearest even)
+ *   workspace     device scratch of >= kvc_decode_workspace_bytes(...) bytes, no
+ *                 initialisation needed; may be NULL when max_context_len fits one
+ *                 partition (the size query then returns 0).
+ * Long contexts are split over several workgroups (split-K) whose partial
+ * softmax states are merged by a second kernel on the same stream. */
+int kvc_paged_decode_attention(const kvc_cache* cache, const void* q, int32_t B, int32_t Hq,
+                               const int32_t* block_table, int32_t max_blocks,
+                               const int32_t* context_lens, int32_t max_context_len,
+                               float softmax_scale, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Chunked prefill: write a prompt chunk's K/V into the cache, then causal
+ * attention of each chunk position over the cached prefix plus the chunk's
+ * positions up to and including itself.
+ *   q             device [total_tokens][Hq][head_dim], chunks of all sequences
+ *                 packed back to back
+ *   k, v          device [total_tokens][num_kv_heads][head_dim]: the chunk's K/V
+ *   cu_chunk_lens device int32 [n_seqs + 1]: chunk i is rows cu[i] .. cu[i+1]-1
+ *   prefix_lens   device int32 [n_seqs]: tokens already cached before the chunk
+ *                 (the chunk covers positions prefix .. prefix + C - 1)
+ *   block_table   device int32 [n_seqs][max_blocks], covering prefix + chunk
+ *   total_tokens, max_chunk_len  host-known: cu[n_seqs] and max_i C_i
+ *   out           device [total_tokens][Hq][head_dim], cache dtype
+ * The K/V write completes before the attention reads (same stream). */
+int kvc_chunked_prefill_attention(const kvc_cache* cache, const void* q, const void* k,
+                                  const void* v, int32_t n_seqs, const int32_t* cu_chunk_lens,
+                                  const int32_t* prefix_lens, int32_t total_tokens,
+                                  int32_t max_chunk_len, const int32_t* block_table,
+                                  int32_t max_blocks, int32_t Hq, float softmax_scale,
+                                  void* out, void* stream);
+
+/* Static string for a status code. */
+const char* kvc_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

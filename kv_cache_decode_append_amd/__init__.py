@@ -1,0 +1,23 @@
+"""Paged KV-cache append, GQA decode attention and chunked-prefill attention on
+AMD MI355X (gfx950): HIP kernels behind the C ABI in include/kvc.h, with this
+thin binding on top. Importing the package loads libkvc.so and raises if it is
+missing; there is no CPU fallback.
+"""
+from ._lib import (  # noqa: F401
+    BLOCK_SIZE,
+    DEVERR_BLOCK_ID,
+    DEVERR_CONTEXT,
+    DEVERR_SLOT,
+    KVC_BF16,
+    KVC_F32,
+    LIB,
+    LIB_PATH,
+    KvcError,
+    PagedKVCache,
+    chunked_prefill_attention,
+    decode_workspace_bytes,
+    kv_append,
+    kv_bytes_per_token,
+    paged_decode_attention,
+    slot_mapping,
+)

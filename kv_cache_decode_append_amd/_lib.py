@@ -1,0 +1,259 @@
+"""ctypes binding for libkvc.so: argument marshalling only.
+
+Every function here checks tensor dtypes, devices and shapes, passes raw device
+pointers plus torch's current HIP stream to the C ABI declared in
+include/kvc.h, and raises on a negative status. All computation happens in the
+HIP kernels; there is no fallback path. If the library is missing or cannot be
+loaded, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvc.so")
+
+KVC_F32, KVC_BF16 = 0, 1
+DEVERR_BLOCK_ID, DEVERR_SLOT, DEVERR_CONTEXT = 1, 2, 4
+BLOCK_SIZE = 16
+
+_DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
+
+
+class KvcError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class _CCache(ctypes.Structure):
+    _fields_ = [
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("err_flag", ctypes.c_void_p),
+    ]
+
+
+def _hip_runtimes_mapped() -> set[str]:
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m kv_cache_decode_append_amd.build`")
+    # torch's own HIP runtime must already be mapped so that the library binds
+    # to it (same soname) instead of loading a second runtime.
+    import torch.cuda  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError(f"two HIP runtimes are mapped in this process: {sorted(runtimes)}")
+    c_int, c_i32, c_i64, c_sz = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    vp, fl = ctypes.c_void_p, ctypes.c_float
+    P = ctypes.POINTER(_CCache)
+    sig = {
+        "kvc_kv_bytes_per_token": (c_i64, [c_i32, c_i32, c_i32, c_i32]),
+        "kvc_slot_mapping": (c_int, [vp, c_i32, c_i32, c_i32, vp, vp, c_i32, c_i32, vp, vp, vp]),
+        "kvc_kv_append": (c_int, [P, vp, vp, vp, c_i32, vp]),
+        "kvc_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32]),
+        "kvc_paged_decode_attention": (c_int, [P, vp, c_i32, c_i32, vp, c_i32, vp, c_i32, fl, vp,
+                                               vp, c_sz, vp]),
+        "kvc_chunked_prefill_attention": (c_int, [P, vp, vp, vp, c_i32, vp, vp, c_i32, c_i32, vp,
+                                                  c_i32, c_i32, fl, vp, vp]),
+        "kvc_status_string": (ctypes.c_char_p, [c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+LIB = _load()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise KvcError(fn, status, LIB.kvc_status_string(status).decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+class PagedKVCache:
+    """One layer's K and V block pools, [num_blocks, Hkv, 16, head_dim] each.
+
+    The tensors are owned by the caller (allocated here with torch for
+    convenience); the library only reads and writes them.
+    """
+
+    def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 err_flag: torch.Tensor | None = None):
+        _need(k_cache, "k_cache", ndim=4)
+        _need(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4, device=k_cache.device)
+        if k_cache.shape != v_cache.shape:
+            raise ValueError("k_cache and v_cache shapes differ")
+        if k_cache.dtype not in _DTYPE_CODE:
+            raise TypeError(f"cache dtype {k_cache.dtype} is not fp32 or bf16")
+        if k_cache.shape[2] != BLOCK_SIZE:
+            raise ValueError("block size must be 16")
+        if err_flag is not None:
+            _need(err_flag, "err_flag", dtype=torch.int32, device=k_cache.device)
+        self.k_cache, self.v_cache, self.err_flag = k_cache, v_cache, err_flag
+        nb, hkv, _, d = k_cache.shape
+        self.num_blocks, self.num_kv_heads, self.head_dim = nb, hkv, d
+        self.dtype = k_cache.dtype
+        self._c = _CCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, BLOCK_SIZE, hkv, d,
+                          _DTYPE_CODE[k_cache.dtype], _ptr(err_flag))
+
+    @classmethod
+    def allocate(cls, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
+                 device="cuda", with_err_flag: bool = True, fill_bits: int | None = None):
+        shape = (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim)
+        k = torch.empty(shape, dtype=dtype, device=device)
+        v = torch.empty(shape, dtype=dtype, device=device)
+        if fill_bits is not None:
+            ib = torch.int16 if dtype == torch.bfloat16 else torch.int32
+            k.view(ib).fill_(fill_bits)
+            v.view(ib).fill_(fill_bits)
+        err = torch.zeros(1, dtype=torch.int32, device=device) if with_err_flag else None
+        return cls(k, v, err)
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, dtype_bytes: int) -> int:
+    return int(LIB.kvc_kv_bytes_per_token(layers, kv_heads, head_dim, dtype_bytes))
+
+
+def slot_mapping(block_table: torch.Tensor, num_blocks: int, seq_ids: torch.Tensor,
+                 positions: torch.Tensor, out: torch.Tensor | None = None,
+                 err_flag: torch.Tensor | None = None) -> torch.Tensor:
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_ids, "seq_ids", torch.int32, 1, block_table.device)
+    _need(positions, "positions", torch.int32, 1, block_table.device)
+    T = positions.shape[0]
+    if seq_ids.shape[0] != T:
+        raise ValueError("seq_ids and positions differ in length")
+    if out is None:
+        out = torch.empty(T, dtype=torch.int64, device=block_table.device)
+    _need(out, "slot_mapping", torch.int64, 1, block_table.device)
+    _check("kvc_slot_mapping", LIB.kvc_slot_mapping(
+        block_table.data_ptr(), block_table.shape[0], block_table.shape[1], num_blocks,
+        seq_ids.data_ptr(), positions.data_ptr(), T, BLOCK_SIZE, out.data_ptr(),
+        _ptr(err_flag), _stream()))
+    return out
+
+
+def kv_append(cache: PagedKVCache, slot_mapping: torch.Tensor, k: torch.Tensor,
+              v: torch.Tensor) -> None:
+    _need(slot_mapping, "slot_mapping", torch.int64, 1, cache.k_cache.device)
+    _need(k, "k", cache.dtype, 3, cache.k_cache.device)
+    _need(v, "v", cache.dtype, 3, cache.k_cache.device)
+    T = slot_mapping.shape[0]
+    if k.shape != (T, cache.num_kv_heads, cache.head_dim) or v.shape != k.shape:
+        raise ValueError(f"k/v must be [{T}, {cache.num_kv_heads}, {cache.head_dim}]")
+    _check("kvc_kv_append", LIB.kvc_kv_append(cache.c, slot_mapping.data_ptr(), k.data_ptr(),
+                                              v.data_ptr(), T, _stream()))
+
+
+def decode_workspace_bytes(B: int, Hq: int, head_dim: int, max_context_len: int) -> int:
+    return int(LIB.kvc_decode_workspace_bytes(B, Hq, head_dim, max_context_len))
+
+
+def paged_decode_attention(cache: PagedKVCache, q: torch.Tensor, block_table: torch.Tensor,
+                           context_lens: torch.Tensor, max_context_len: int,
+                           softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    dev = cache.k_cache.device
+    _need(q, "q", cache.dtype, 3, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    if D != cache.head_dim or block_table.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("q / block_table / context_lens shapes disagree")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", cache.dtype, 3, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    need = decode_workspace_bytes(B, Hq, D, max_context_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None:
+        _need(workspace, "workspace", device=dev)
+    scale = (1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
+    _check("kvc_paged_decode_attention", LIB.kvc_paged_decode_attention(
+        cache.c, q.data_ptr(), B, Hq, block_table.data_ptr(), block_table.shape[1],
+        context_lens.data_ptr(), int(max_context_len), scale, out.data_ptr(),
+        _ptr(workspace), ws_bytes, _stream()))
+    return out
+
+
+def chunked_prefill_attention(cache: PagedKVCache, q: torch.Tensor, k: torch.Tensor,
+                              v: torch.Tensor, cu_chunk_lens: torch.Tensor,
+                              prefix_lens: torch.Tensor, block_table: torch.Tensor,
+                              max_chunk_len: int, softmax_scale: float | None = None,
+                              out: torch.Tensor | None = None) -> torch.Tensor:
+    dev = cache.k_cache.device
+    _need(q, "q", cache.dtype, 3, dev)
+    _need(k, "k", cache.dtype, 3, dev)
+    _need(v, "v", cache.dtype, 3, dev)
+    _need(cu_chunk_lens, "cu_chunk_lens", torch.int32, 1, dev)
+    _need(prefix_lens, "prefix_lens", torch.int32, 1, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    total, Hq, D = q.shape
+    n = prefix_lens.shape[0]
+    if cu_chunk_lens.shape[0] != n + 1 or block_table.shape[0] != n:
+        raise ValueError("cu_chunk_lens / prefix_lens / block_table disagree on n_seqs")
+    if k.shape != (total, cache.num_kv_heads, D) or v.shape != k.shape or D != cache.head_dim:
+        raise ValueError("k / v must be [total_tokens, Hkv, head_dim]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", cache.dtype, 3, dev)
+    scale = (1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
+    _check("kvc_chunked_prefill_attention", LIB.kvc_chunked_prefill_attention(
+        cache.c, q.data_ptr(), k.data_ptr(), v.data_ptr(), n, cu_chunk_lens.data_ptr(),
+        prefix_lens.data_ptr(), total, int(max_chunk_len), block_table.data_ptr(),
+        block_table.shape[1], Hq, scale, out.data_ptr(), _stream()))
+    return out

@@ -1,0 +1,149 @@
+// Slot mapping and KV append.
+//
+// A decode step appends the new position's key and value to the cache before
+// attending over everything stored (aiwithghost.com "KV cache and continuous
+// batching: 1,000 people ask AI", section "What does a KV cache keep?";
+// daviddominguez.dev "The KV cache and prefix caching", section "What prefill
+// stores and decode reads"). The cache is paged: fixed 16-token blocks reached
+// through a per-sequence block table (daviddominguez.dev, same section and
+// section "A prefix already in the cache can skip its prefill").
+//
+// Both kernels are pure integer work / byte copies: bit-exact by construction.
+// The append is HBM-bound and tiny (one 16-byte chunk per lane, each token row
+// of one head is `head_dim * elem` contiguous bytes on both sides).
+
+#include "kvc_append.h"
+#include "kvc_device.h"
+#include "kvc_host.h"
+
+namespace kvc {
+
+__global__ void slot_mapping_kernel(const int32_t* __restrict__ block_table, int32_t n_seqs,
+                                    int32_t max_blocks,
+                                    int32_t num_blocks, const int32_t* __restrict__ seq_ids,
+                                    const int32_t* __restrict__ positions, int32_t T,
+                                    int64_t* __restrict__ slots, int32_t* err) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const int32_t p = positions[t];
+  int64_t slot = -1;
+  const int32_t sid = seq_ids[t];
+  if (p >= 0) {
+    const int32_t lb = p >> 4;
+    if (lb >= max_blocks || sid < 0 || sid >= n_seqs) {
+      flag_error(err, KVC_DEVERR_CONTEXT);
+    } else {
+      const int32_t blk = block_table[(int64_t)sid * max_blocks + lb];
+      if (blk < 0 || blk >= num_blocks)
+        flag_error(err, KVC_DEVERR_BLOCK_ID);
+      else
+        slot = (int64_t)blk * 16 + (p & 15);
+    }
+  }
+  slots[t] = slot;
+}
+
+// One 16-byte chunk of K and of V per thread.
+// chunk id -> (token t, kv head h, chunk c), rows are `nc` chunks long.
+__global__ void kv_append_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                 const int64_t* __restrict__ slots,
+                                 const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+                                 int64_t n_chunks, int32_t hkv, int32_t nc,
+                                 int64_t num_slots, int32_t* err) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_chunks) return;
+  const int64_t row = i / nc;          // (t, h)
+  const int32_t c = (int32_t)(i - row * nc);
+  const int64_t t = row / hkv;
+  const int32_t h = (int32_t)(row - t * hkv);
+  const int64_t slot = slots[t];
+  if (slot < 0) return;
+  if (slot >= num_slots) {
+    if (h == 0 && c == 0) flag_error(err, KVC_DEVERR_SLOT);
+    return;
+  }
+  const int64_t blk = slot >> 4, off = slot & 15;
+  const int64_t row_bytes = (int64_t)nc * 16;
+  const int64_t dst = ((blk * hkv + h) * 16 + off) * row_bytes + (int64_t)c * 16;
+  const int64_t src = i * 16;
+  *reinterpret_cast<u32x4*>(kc + dst) = *reinterpret_cast<const u32x4*>(k + src);
+  *reinterpret_cast<u32x4*>(vc + dst) = *reinterpret_cast<const u32x4*>(v + src);
+}
+
+// Prefill-chunk write: token r of sequence s (r < C_s) goes to position
+// prefix_s + r. grid = (ceil(max_chunk * hkv * nc / 256), n_seqs).
+__global__ void chunk_append_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                    const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+                                    const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
+                                    const int32_t* __restrict__ block_table, int32_t max_blocks,
+                                    int32_t num_blocks, int32_t hkv, int32_t nc, int32_t* err) {
+  const int s = blockIdx.y;
+  const int32_t t0 = cu[s], C = cu[s + 1] - t0, p0 = prefix[s];
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)C * hkv * nc) return;
+  const int64_t row = i / nc;
+  const int32_t c = (int32_t)(i - row * nc);
+  const int32_t r = (int32_t)(row / hkv);
+  const int32_t h = (int32_t)(row - (int64_t)r * hkv);
+  const int32_t p = p0 + r;
+  const int32_t lb = p >> 4;
+  if (lb >= max_blocks) {
+    if (h == 0 && c == 0) flag_error(err, KVC_DEVERR_CONTEXT);
+    return;
+  }
+  const int32_t blk = block_table[(int64_t)s * max_blocks + lb];
+  if (blk < 0 || blk >= num_blocks) {
+    if (h == 0 && c == 0) flag_error(err, KVC_DEVERR_BLOCK_ID);
+    return;
+  }
+  const int64_t row_bytes = (int64_t)nc * 16;
+  const int64_t dst = (((int64_t)blk * hkv + h) * 16 + (p & 15)) * row_bytes + (int64_t)c * 16;
+  const int64_t src = (((int64_t)(t0 + r) * hkv + h) * nc + c) * 16;
+  *reinterpret_cast<u32x4*>(kc + dst) = *reinterpret_cast<const u32x4*>(k + src);
+  *reinterpret_cast<u32x4*>(vc + dst) = *reinterpret_cast<const u32x4*>(v + src);
+}
+
+int launch_chunk_append(const kvc_cache* c, const void* k, const void* v, int32_t n_seqs,
+                        const int32_t* cu, const int32_t* prefix, int32_t max_chunk,
+                        const int32_t* block_table, int32_t max_blocks, hipStream_t st) {
+  const int nc = c->head_dim * dtype_bytes(c->dtype) / 16;
+  const int64_t per_seq = (int64_t)max_chunk * c->num_kv_heads * nc;
+  if (per_seq == 0 || n_seqs == 0) return KVC_OK;
+  dim3 grid((unsigned)ceil_div(per_seq, 256), (unsigned)n_seqs);
+  hipLaunchKernelGGL(chunk_append_kernel, grid, dim3(256), 0, st, (uint8_t*)c->k_cache,
+                     (uint8_t*)c->v_cache, (const uint8_t*)k, (const uint8_t*)v, cu, prefix,
+                     block_table, max_blocks, c->num_blocks, c->num_kv_heads, nc, c->err_flag);
+  return launch_status();
+}
+
+}  // namespace kvc
+
+extern "C" int kvc_slot_mapping(const int32_t* block_table, int32_t n_seqs, int32_t max_blocks,
+                                int32_t num_blocks, const int32_t* seq_ids, const int32_t* positions, int32_t T,
+                                int32_t block_size, int64_t* slot_mapping, int32_t* err_flag,
+                                void* stream) {
+  if (T < 0 || n_seqs < 0 || max_blocks < 0 || num_blocks < 0) return KVC_ERR_SHAPE;
+  if (block_size != 16) return KVC_ERR_UNSUPPORTED;
+  if (T == 0) return KVC_OK;
+  if (!block_table || !seq_ids || !positions || !slot_mapping) return KVC_ERR_NULL;
+  hipLaunchKernelGGL(kvc::slot_mapping_kernel, dim3((unsigned)kvc::ceil_div(T, 256)), dim3(256), 0,
+                     kvc::as_stream(stream), block_table, n_seqs, max_blocks, num_blocks, seq_ids,
+                     positions, T, slot_mapping, err_flag);
+  return kvc::launch_status();
+}
+
+extern "C" int kvc_kv_append(const kvc_cache* cache, const int64_t* slot_mapping, const void* k,
+                             const void* v, int32_t T, void* stream) {
+  int st = kvc::check_cache(cache);
+  if (st != KVC_OK) return st;
+  if (T < 0) return KVC_ERR_SHAPE;
+  if (T == 0) return KVC_OK;
+  if (!slot_mapping || !k || !v) return KVC_ERR_NULL;
+  const int nc = cache->head_dim * kvc::dtype_bytes(cache->dtype) / 16;
+  const int64_t n_chunks = (int64_t)T * cache->num_kv_heads * nc;
+  hipLaunchKernelGGL(kvc::kv_append_kernel, dim3((unsigned)kvc::ceil_div(n_chunks, 256)), dim3(256),
+                     0, kvc::as_stream(stream), (uint8_t*)cache->k_cache, (uint8_t*)cache->v_cache,
+                     slot_mapping, (const uint8_t*)k, (const uint8_t*)v, n_chunks,
+                     cache->num_kv_heads, nc, (int64_t)cache->num_blocks * 16, cache->err_flag);
+  return kvc::launch_status();
+}

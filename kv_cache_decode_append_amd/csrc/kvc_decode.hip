@@ -1,0 +1,477 @@
+// Paged GQA decode attention with split-K over the context and a merge pass.
+//
+// Each decode step attends the new query over every key and value stored for its
+// sequence (aiwithghost.com "KV cache and continuous batching: 1,000 people ask
+// AI", section "What does a KV cache keep?"; daviddominguez.dev "The KV cache
+// and prefix caching", section "What prefill stores and decode reads"), reading
+// them through the sequence's block table (same page, PagedAttention design),
+// with several query heads sharing one K/V head (same page, grouped-query
+// attention). The read of the whole cache is what grows with context (same page,
+// section "The prompt is paid once, the output is paid every step"), so this
+// kernel is HBM-bound: it is built to stream K/V at full bandwidth.
+//
+// Work decomposition (one workgroup = 4 waves):
+//   grid = (partition, kv_head, sequence). A partition is `part_blocks`
+//   consecutive 16-token blocks of one sequence. Wave w of the workgroup walks
+//   blocks w, w+4, w+8, ... of the partition on its own (no barriers in the main
+//   loop), keeping an online-softmax state (m, l, acc) for the G query heads of
+//   its kv head, so every K/V tile is read from HBM exactly once per kv head.
+//   At the end the four wave states are merged in LDS; a sequence that spans
+//   several partitions writes (m, l, acc) partials that decode_merge_kernel
+//   combines with the log-sum-exp rule.
+//
+// Per block (one contiguous (block, kv-head) tile of 16 x head_dim for K and for V):
+//   * K and V tiles arrive through 16-byte buffer loads, double-buffered in
+//     registers one block ahead. A buffer descriptor of zero bytes turns the
+//     prefetch past the wave's last block into a no-op with no memory traffic.
+//   * QK: K goes to a per-wave LDS tile with an XOR swizzle of its 16-byte
+//     chunks (conflict-free row reads); lane (h, t) computes the full dot product
+//     of query head h with token t's key (bf16: v_dot2_f32_bf16, fp32: FMA), so
+//     no cross-lane sum is needed. Scores are in the log2 domain (scale*log2 e).
+//   * softmax: max and sum over the 16 tokens of a head are DPP reductions
+//     inside a row of 16 lanes (8 lanes x 2 for G = 8).
+//   * PV: lane owns one 16-byte chunk of a V row and accumulates all G heads;
+//     the accumulator is rescaled only when some head's running max moved.
+
+#include <math.h>
+
+#include "kvc_device.h"
+#include "kvc_host.h"
+
+namespace kvc {
+
+constexpr int kWaves = 4;
+constexpr int kMinPartBlocks = 16;
+
+template <typename T, int D, int G>
+struct DecodeShape {
+  static constexpr int EB = ElemBytes<T>::value;
+  static constexpr int RB = D * EB;             // bytes of one token row of one head
+  static constexpr int NC = RB / 16;            // 16-byte chunks per row
+  static constexpr int CE = 16 / EB;            // elements per chunk
+  static constexpr int TILE = 16 * RB;          // one (block, kv head) tile, bytes
+  static constexpr int LPH = (G == 8) ? 8 : 16; // QK lanes per query head
+  static constexpr int SPL = 16 / LPH;          // tokens per QK lane per block
+  static constexpr int TPI = 64 / NC;           // V tokens covered by one wave load
+  static constexpr int NI = NC / 4;             // 16-byte loads per lane per tile
+  static constexpr int KST = kWaves * TILE;     // K staging, all waves
+  static constexpr int RED = kWaves * TPI * G * D * 4;   // end-of-kernel reduction
+  static constexpr int AREA = KST > RED ? KST : RED;
+  static constexpr int SMEM = AREA + kWaves * 16 * G * 4 + kWaves * G * 8;
+  static_assert(NC >= 4 && NC <= 64, "row of 64..1024 bytes");
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "G in {1,2,4,8}");
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* bt;
+  const int32_t* ctx_lens;
+  void* out;
+  float* ws_o;        // [B*Hq][n_part][D]
+  float2* ws_ml;      // [B*Hq][n_part]
+  int32_t* err;
+  int32_t hkv;
+  int32_t num_blocks;
+  int32_t max_blocks;
+  int32_t max_ctx;
+  int32_t part_blocks;
+  int32_t n_part;
+  float scale_log2;   // softmax scale * log2(e)
+};
+
+// Context length the kernels use: clamped to what the grid and table cover.
+__device__ __forceinline__ int effective_ctx(const DecodeArgs& a, int b, bool report) {
+  int ctx = a.ctx_lens[b];
+  const int cap = min(a.max_ctx, a.max_blocks * 16);
+  if (ctx > cap || ctx < 0) {
+    if (report) flag_error(a.err, KVC_DEVERR_CONTEXT);
+    ctx = ctx < 0 ? 0 : cap;
+  }
+  return ctx;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out(void* out, size_t idx, float x);
+template <>
+__device__ __forceinline__ void store_out<float>(void* out, size_t idx, float x) {
+  reinterpret_cast<float*>(out)[idx] = x;
+}
+template <>
+__device__ __forceinline__ void store_out<bf16_tag>(void* out, size_t idx, float x) {
+  reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)f32_to_bf16_bits(x);
+}
+
+// Dot product of one 16-byte chunk pair, 4 independent partial sums.
+template <typename T>
+__device__ __forceinline__ void chunk_dot(const u32x4& k, const u32x4& q, float (&s)[4]);
+template <>
+__device__ __forceinline__ void chunk_dot<bf16_tag>(const u32x4& k, const u32x4& q, float (&s)[4]) {
+  s[0] = dot2_bf16(k.x, q.x, s[0]);
+  s[1] = dot2_bf16(k.y, q.y, s[1]);
+  s[2] = dot2_bf16(k.z, q.z, s[2]);
+  s[3] = dot2_bf16(k.w, q.w, s[3]);
+}
+template <>
+__device__ __forceinline__ void chunk_dot<float>(const u32x4& k, const u32x4& q, float (&s)[4]) {
+  s[0] = fmaf(__uint_as_float(k.x), __uint_as_float(q.x), s[0]);
+  s[1] = fmaf(__uint_as_float(k.y), __uint_as_float(q.y), s[1]);
+  s[2] = fmaf(__uint_as_float(k.z), __uint_as_float(q.z), s[2]);
+  s[3] = fmaf(__uint_as_float(k.w), __uint_as_float(q.w), s[3]);
+}
+
+// Unpack a 16-byte chunk into CE fp32 values.
+template <typename T, int CE>
+__device__ __forceinline__ void unpack(const u32x4& v, float (&x)[CE]);
+template <>
+__device__ __forceinline__ void unpack<bf16_tag, 8>(const u32x4& v, float (&x)[8]) {
+  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+  x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+  x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+template <>
+__device__ __forceinline__ void unpack<float, 4>(const u32x4& v, float (&x)[4]) {
+  x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+  x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a) {
+  using S = DecodeShape<T, D, G>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
+
+  const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hq_all = a.hkv * G;
+
+  const int ctx = effective_ctx(a, b, part == 0 && kvh == 0 && tid == 0);
+  const int nblk = (ctx + 15) >> 4;
+  const int n_used = nblk > 0 ? (nblk + a.part_blocks - 1) / a.part_blocks : 1;
+  if (part >= n_used) return;
+  if (ctx == 0) {
+    for (int o = tid; o < G * D; o += kWaves * 64)
+      store_out<T>(a.out, ((size_t)b * hq_all + kvh * G) * D + o, 0.f);
+    return;
+  }
+  const int blk0 = part * a.part_blocks;
+  const int blk_end = min(blk0 + a.part_blocks, nblk);
+  const int n_my = (blk_end - blk0 > w) ? (blk_end - blk0 - w + kWaves - 1) / kWaves : 0;
+
+  uint8_t* kst = smem + w * S::TILE;
+  float* plds = reinterpret_cast<float*>(smem + S::AREA) + w * 16 * G;
+  float2* ml = reinterpret_cast<float2*>(smem + S::AREA + kWaves * 16 * G * 4);
+
+  // QK layout: lane -> (head h, token slot tq)
+  const int h = lane / S::LPH, tq = lane % S::LPH;
+  const bool active = h < G;
+  u32x4 qv[S::NC];
+  {
+    const int hq = kvh * G + (active ? h : 0);
+    const u32x4* qp = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const uint8_t*>(a.q) + ((size_t)b * hq_all + hq) * S::RB);
+#pragma unroll
+    for (int c = 0; c < S::NC; ++c) qv[c] = qp[c];
+  }
+
+  const int32_t* bt_row = a.bt + (size_t)b * a.max_blocks;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kc);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vc);
+
+  // Issue the loads of this wave's i-th block into (kb, vb).
+  auto issue = [&](u32x4 (&kb)[S::NI], u32x4 (&vb)[S::NI], int i) {
+    size_t off = 0;
+    uint32_t bytes = 0;
+    if (i < n_my) {
+      int blk = __builtin_amdgcn_readfirstlane(bt_row[blk0 + w + i * kWaves]);
+      if ((unsigned)blk < (unsigned)a.num_blocks) {
+        off = ((size_t)blk * a.hkv + kvh) * S::TILE;
+        bytes = S::TILE;
+      } else if (lane == 0) {
+        flag_error(a.err, KVC_DEVERR_BLOCK_ID);
+      }
+    }
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + off, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + off, bytes);
+#pragma unroll
+    for (int j = 0; j < S::NI; ++j) kb[j] = buffer_load16(rk, (uint32_t)(j * 64 + lane) * 16u);
+#pragma unroll
+    for (int j = 0; j < S::NI; ++j) vb[j] = buffer_load16(rv, (uint32_t)(j * 64 + lane) * 16u);
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[G][S::CE];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int e = 0; e < S::CE; ++e) acc[hh][e] = 0.f;
+
+  auto process = [&](const u32x4 (&kb)[S::NI], const u32x4 (&vb)[S::NI], int i) {
+    const int lb = blk0 + w + i * kWaves;
+    // K tile -> LDS, chunk c of token t at chunk slot c ^ (t % NC)
+#pragma unroll
+    for (int j = 0; j < S::NI; ++j) {
+      const int ci = j * 64 + lane, tk = ci / S::NC, c = ci % S::NC;
+      *reinterpret_cast<u32x4*>(kst + tk * S::RB + ((c ^ (tk % S::NC)) << 4)) = kb[j];
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    float s[S::SPL];
+#pragma unroll
+    for (int sl = 0; sl < S::SPL; ++sl) {
+      const int t = tq + S::LPH * sl;
+      float part_s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < S::NC; ++c) {
+        const u32x4 kk = *reinterpret_cast<const u32x4*>(kst + t * S::RB + ((c ^ (t % S::NC)) << 4));
+        chunk_dot<T>(kk, qv[c], part_s);
+      }
+      const float sc = ((part_s[0] + part_s[1]) + (part_s[2] + part_s[3])) * a.scale_log2;
+      s[sl] = (active && lb * 16 + t < ctx) ? sc : -INFINITY;
+    }
+
+    // online softmax over this block's tokens, per head
+    float mx = s[0];
+#pragma unroll
+    for (int sl = 1; sl < S::SPL; ++sl) mx = fmaxf(mx, s[sl]);
+    mx = group_max<S::LPH>(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_safe);
+    float p[S::SPL], ps = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < S::SPL; ++sl) {
+      p[sl] = __builtin_amdgcn_exp2f(s[sl] - m_safe);
+      ps += p[sl];
+    }
+    ps = group_sum<S::LPH>(ps);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    if (active) {
+#pragma unroll
+      for (int sl = 0; sl < S::SPL; ++sl) plds[(tq + S::LPH * sl) * G + h] = p[sl];
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // rescale the accumulators when a running max moved
+    float al[G];
+    bool moved = false;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      al[hh] = readlane_f(alpha, hh * S::LPH);
+      moved |= (al[hh] != 1.f);
+    }
+    if (moved) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < S::CE; ++e) acc[hh][e] *= al[hh];
+    }
+
+    // PV: lane owns chunk (lane % NC) of token j*TPI + lane / NC
+    const bool tail = (lb == nblk - 1) && ((ctx & 15) != 0);
+#pragma unroll
+    for (int j = 0; j < S::NI; ++j) {
+      const int tv = j * S::TPI + lane / S::NC;
+      float pv[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) pv[hh] = plds[tv * G + hh];
+      u32x4 vv = vb[j];
+      if (tail && lb * 16 + tv >= ctx) vv = u32x4{0u, 0u, 0u, 0u};   // unwritten rows may hold NaN
+      float x[S::CE];
+      unpack<T, S::CE>(vv, x);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < S::CE; ++e) acc[hh][e] = fmaf(pv[hh], x[e], acc[hh][e]);
+    }
+  };
+
+  {
+    u32x4 kb0[S::NI], vb0[S::NI], kb1[S::NI], vb1[S::NI];
+    issue(kb0, vb0, 0);
+    issue(kb1, vb1, 1);
+    for (int i = 0; i < n_my; i += 2) {
+      process(kb0, vb0, i);
+      issue(kb0, vb0, i + 2);
+      if (i + 1 < n_my) process(kb1, vb1, i + 1);
+      issue(kb1, vb1, i + 3);
+    }
+  }
+
+  // merge the four wave states
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);   // [kWaves][TPI][G][D]
+  {
+    const int sub = lane / S::NC, cc = lane % S::NC;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float* dst = red + ((w * S::TPI + sub) * G + hh) * D + cc * S::CE;
+#pragma unroll
+      for (int e = 0; e < S::CE; e += 4)
+        *reinterpret_cast<f32x4*>(dst + e) = f32x4{acc[hh][e], acc[hh][e + 1], acc[hh][e + 2], acc[hh][e + 3]};
+    }
+    if (active && tq == 0) ml[w * G + h] = make_float2(m_run, l_run);
+  }
+  __syncthreads();
+  for (int o = tid; o < G * D; o += kWaves * 64) {
+    const int hh = o / D, d = o % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, ml[ww * G + hh].x);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float2 st = ml[ww * G + hh];
+      const float f = (st.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.x - M);
+      float sum = 0.f;
+#pragma unroll
+      for (int sub = 0; sub < S::TPI; ++sub) sum += red[((ww * S::TPI + sub) * G + hh) * D + d];
+      L += st.y * f;
+      A += sum * f;
+    }
+    const size_t row = (size_t)b * hq_all + kvh * G + hh;
+    if (n_used == 1) {
+      store_out<T>(a.out, row * D + d, A / L);
+    } else {
+      a.ws_o[(row * a.n_part + part) * D + d] = A;
+      if (d == 0) a.ws_ml[row * a.n_part + part] = make_float2(M, L);
+    }
+  }
+}
+
+// One wave per (sequence, query head): combine the partition partials.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int32_t hq_all) {
+  const int row = blockIdx.x;                 // b * Hq + hq
+  const int b = row / hq_all;
+  const int ctx = effective_ctx(a, b, false);
+  const int nblk = (ctx + 15) >> 4;
+  const int n_used = nblk > 0 ? (nblk + a.part_blocks - 1) / a.part_blocks : 1;
+  if (n_used <= 1) return;
+  const float2* ml = a.ws_ml + (size_t)row * a.n_part;
+  float M = -INFINITY;
+  for (int i = 0; i < n_used; ++i) M = fmaxf(M, ml[i].x);
+  float L = 0.f;
+  for (int i = 0; i < n_used; ++i) L += ml[i].y * __builtin_amdgcn_exp2f(ml[i].x - M);
+  const float inv = 1.f / L;
+  for (int d = threadIdx.x; d < D; d += 64) {
+    float A = 0.f;
+    for (int i = 0; i < n_used; ++i)
+      A += __builtin_amdgcn_exp2f(ml[i].x - M) * a.ws_o[((size_t)row * a.n_part + i) * D + d];
+    store_out<T>(a.out, (size_t)row * D + d, A * inv);
+  }
+}
+
+template <typename T, int D, int G>
+int launch_decode(const DecodeArgs& a, int B, hipStream_t st) {
+  hipLaunchKernelGGL((paged_decode_kernel<T, D, G>), dim3(a.n_part, a.hkv, B), dim3(kWaves * 64), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return KVC_ERR_LAUNCH;
+  if (a.n_part > 1) {
+    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(B * a.hkv * G), dim3(64), 0, st, a, a.hkv * G);
+    if (hipGetLastError() != hipSuccess) return KVC_ERR_LAUNCH;
+  }
+  return KVC_OK;
+}
+
+template <typename T, int D>
+int dispatch_g(const DecodeArgs& a, int B, int G, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_decode<T, D, 1>(a, B, st);
+    case 2: return launch_decode<T, D, 2>(a, B, st);
+    case 4: return launch_decode<T, D, 4>(a, B, st);
+    case 8: return launch_decode<T, D, 8>(a, B, st);
+  }
+  return KVC_ERR_UNSUPPORTED;
+}
+
+int dispatch_decode(const DecodeArgs& a, int dtype, int D, int B, int G, hipStream_t st) {
+  if (dtype == KVC_F32) {
+    switch (D) {
+      case 16: return dispatch_g<float, 16>(a, B, G, st);
+      case 32: return dispatch_g<float, 32>(a, B, G, st);
+      case 64: return dispatch_g<float, 64>(a, B, G, st);
+      case 128: return dispatch_g<float, 128>(a, B, G, st);
+    }
+  } else {
+    switch (D) {
+      case 32: return dispatch_g<bf16_tag, 32>(a, B, G, st);
+      case 64: return dispatch_g<bf16_tag, 64>(a, B, G, st);
+      case 128: return dispatch_g<bf16_tag, 128>(a, B, G, st);
+    }
+  }
+  return KVC_ERR_UNSUPPORTED;
+}
+
+// Blocks per partition: aim for >= 2048 workgroups (8 per CU) so the grid
+// fills all 256 CUs several times over, but never fewer than 16 blocks (4 per
+// wave) so each wave's prefetch pipeline has work to overlap.
+int decode_part_blocks(int B, int hkv, int nblk_max) {
+  static const int forced = [] {
+    const char* e = getenv("KVC_DECODE_PART_BLOCKS");
+    return e ? atoi(e) : 0;
+  }();
+  if (forced >= kMinPartBlocks) return forced;
+  const int64_t units = (int64_t)B * hkv;
+  const int64_t want = units >= 2048 ? 1 : (2048 + units - 1) / units;
+  int64_t pb = (nblk_max + want - 1) / want;
+  pb = (pb + 3) / 4 * 4;
+  if (pb < kMinPartBlocks) pb = kMinPartBlocks;
+  return (int)pb;
+}
+
+}  // namespace kvc
+
+extern "C" size_t kvc_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim,
+                                             int32_t max_context_len) {
+  if (B <= 0 || Hq <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  const int64_t nblk = kvc::ceil_div(max_context_len, 16);
+  const int64_t n_part_max = kvc::ceil_div(nblk, kvc::kMinPartBlocks);
+  if (n_part_max <= 1) return 0;
+  return (size_t)B * Hq * n_part_max * ((size_t)head_dim * 4 + 8);
+}
+
+extern "C" int kvc_paged_decode_attention(const kvc_cache* cache, const void* q, int32_t B, int32_t Hq,
+                                          const int32_t* block_table, int32_t max_blocks,
+                                          const int32_t* context_lens, int32_t max_context_len,
+                                          float softmax_scale, void* out, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  int st = kvc::check_cache(cache);
+  if (st != KVC_OK) return st;
+  if (B < 0 || Hq <= 0 || max_blocks < 0 || max_context_len < 0) return KVC_ERR_SHAPE;
+  if (Hq % cache->num_kv_heads != 0) return KVC_ERR_SHAPE;
+  const int G = Hq / cache->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KVC_ERR_UNSUPPORTED;
+  if ((int64_t)max_context_len > (int64_t)max_blocks * 16) return KVC_ERR_SHAPE;
+  if (B == 0) return KVC_OK;
+  if (!q || !block_table || !context_lens || !out) return KVC_ERR_NULL;
+
+  const int nblk_max = (int)kvc::ceil_div(max_context_len, 16);
+  const int pb = kvc::decode_part_blocks(B, cache->num_kv_heads, nblk_max);
+  const int n_part = nblk_max > 0 ? (int)kvc::ceil_div(nblk_max, pb) : 1;
+  const size_t n_rows = (size_t)B * Hq * n_part;
+  const size_t need = n_part > 1 ? n_rows * ((size_t)cache->head_dim * 4 + 8) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KVC_ERR_WORKSPACE;
+
+  kvc::DecodeArgs a;
+  a.q = q;
+  a.kc = cache->k_cache;
+  a.vc = cache->v_cache;
+  a.bt = block_table;
+  a.ctx_lens = context_lens;
+  a.out = out;
+  a.ws_o = reinterpret_cast<float*>(workspace);
+  a.ws_ml = need ? reinterpret_cast<float2*>(reinterpret_cast<uint8_t*>(workspace) +
+                                             n_rows * cache->head_dim * 4)
+                 : nullptr;
+  a.err = cache->err_flag;
+  a.hkv = cache->num_kv_heads;
+  a.num_blocks = cache->num_blocks;
+  a.max_blocks = max_blocks;
+  a.max_ctx = max_context_len;
+  a.part_blocks = pb;
+  a.n_part = n_part;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return kvc::dispatch_decode(a, cache->dtype, cache->head_dim, B, G, kvc::as_stream(stream));
+}

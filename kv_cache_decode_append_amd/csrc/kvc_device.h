@@ -1,0 +1,99 @@
+// Device-side helpers shared by the kvc kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Storage tag for bfloat16 elements (raw 16-bit patterns).
+struct bf16_tag {};
+
+template <typename T> struct ElemBytes;
+template <> struct ElemBytes<float> { static constexpr int value = 4; };
+template <> struct ElemBytes<bf16_tag> { static constexpr int value = 2; };
+
+// ---------------------------------------------------------------------------
+// Buffer resources. A raw (stride 0) buffer descriptor over [base, base+bytes):
+// loads at offsets >= bytes return zero and touch no memory, so a descriptor of
+// 0 bytes turns a load into a no-op. Word 3 = 0x00020000 selects the 32-bit
+// raw data format on gfx9-family parts (CDNA included).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           (int)0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions with DPP inside a row of 16 lanes.
+// All lanes of the group end with the group's result.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141; // lane i <-> 7-i within each 8
+constexpr int kRowMirror = 0x140;     // lane i <-> 15-i within each 16
+
+// Reduce over an aligned group of N lanes, N in {8, 16}.
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  v = fmaxf(v, dpp_f<kQuadXor1>(v));
+  v = fmaxf(v, dpp_f<kQuadXor2>(v));
+  v = fmaxf(v, dpp_f<kRowHalfMirror>(v));
+  if constexpr (N == 16) v = fmaxf(v, dpp_f<kRowMirror>(v));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  v += dpp_f<kQuadXor1>(v);
+  v += dpp_f<kQuadXor2>(v);
+  v += dpp_f<kRowHalfMirror>(v);
+  if constexpr (N == 16) v += dpp_f<kRowMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ void flag_error(int32_t* err, int32_t bit) {
+  if (err) atomicOr(err, bit);
+}
+
+}  // namespace kvc

@@ -1,0 +1,41 @@
+// Host-side helpers shared by the kvc C-ABI entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+inline int dtype_bytes(int32_t dtype) {
+  return dtype == KVC_F32 ? 4 : dtype == KVC_BF16 ? 2 : 0;
+}
+
+inline bool head_dim_supported(int32_t dtype, int32_t d) {
+  if (dtype == KVC_F32) return d == 16 || d == 32 || d == 64 || d == 128;
+  if (dtype == KVC_BF16) return d == 32 || d == 64 || d == 128;
+  return false;
+}
+
+// Validates a cache descriptor; returns KVC_OK or a negative status.
+inline int check_cache(const kvc_cache* c) {
+  if (!c || !c->k_cache || !c->v_cache) return KVC_ERR_NULL;
+  if (dtype_bytes(c->dtype) == 0) return KVC_ERR_DTYPE;
+  if (c->block_size != 16) return KVC_ERR_UNSUPPORTED;
+  if (c->num_blocks < 0 || c->num_kv_heads <= 0) return KVC_ERR_SHAPE;
+  if (!head_dim_supported(c->dtype, c->head_dim)) return KVC_ERR_UNSUPPORTED;
+  // 32-bit slot numbers and per-tile byte offsets
+  if ((int64_t)c->num_blocks * c->block_size > INT32_MAX) return KVC_ERR_SHAPE;
+  return KVC_OK;
+}
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_LAUNCH;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace kvc

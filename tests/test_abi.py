@@ -1,0 +1,109 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/kvc.h declares, its host-only functions give the pages' numbers, and bad
+arguments are rejected before any launch (no call here reaches a kernel)."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+kvc = pytest.importorskip("kv_cache_decode_append_amd")
+LIB = kvc.LIB
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"kvc_kv_append", "kvc_paged_decode_attention", "kvc_chunked_prefill_attention",
+            "kvc_slot_mapping"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", kvc.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kvc_[a-z0-9_]+)", out))
+    assert set(names) <= exported, set(names) - exported
+    for n in names:
+        assert hasattr(LIB, n)
+
+
+def test_kv_bytes_per_token_matches_pages():
+    with open(os.path.join(ROOT, "tests", "golden", "page_numbers.json")) as f:
+        page = json.load(f)
+    e = page["kv_bytes_per_token"]
+    assert kvc.kv_bytes_per_token(**e["args"]) == e["value"]
+    e = page["kv_heads_32_kib_per_token"]
+    assert kvc.kv_bytes_per_token(**e["args"]) == e["value"] * 1024
+    assert kvc.kv_bytes_per_token(-1, 8, 128, 2) == -1
+
+
+def test_workspace_size_closed_form():
+    # one partition (<= 16 blocks) needs none
+    assert kvc.decode_workspace_bytes(64, 32, 128, 256) == 0
+    # 32,000 tokens = 2,000 blocks -> at most 125 partitions of >= 16 blocks
+    assert kvc.decode_workspace_bytes(8, 32, 128, 32000) == 8 * 32 * 125 * (128 * 4 + 8)
+    assert kvc.decode_workspace_bytes(0, 32, 128, 32000) == 0
+
+
+def _cache(**over):
+    c = kvc._lib._CCache(1, 1, 8, 16, 4, 16, kvc.KVC_F32, None)
+    for k, v in over.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(k_cache=None), -1),
+    (dict(dtype=7), -3),
+    (dict(block_size=32), -4),
+    (dict(head_dim=48), -4),
+    (dict(num_kv_heads=0), -2),
+])
+def test_bad_cache_rejected_before_launch(over, status):
+    c = _cache(**over)
+    assert LIB.kvc_kv_append(ctypes.byref(c), 1, 1, 1, 4, None) == status
+    assert LIB.kvc_paged_decode_attention(ctypes.byref(c), 1, 1, 4, 1, 4, 1, 64, 0.25, 1,
+                                          None, 0, None) == status
+
+
+def test_bad_shapes_rejected_before_launch():
+    c = _cache()
+    byref = ctypes.byref(c)
+    # Hq not a multiple of Hkv
+    assert LIB.kvc_paged_decode_attention(byref, 1, 1, 6, 1, 4, 1, 64, 0.25, 1, None, 0, None) == -2
+    # G = 3 is not supported
+    assert LIB.kvc_paged_decode_attention(byref, 1, 1, 12, 1, 4, 1, 64, 0.25, 1, None, 0, None) == -4
+    # context longer than the block table
+    assert LIB.kvc_paged_decode_attention(byref, 1, 1, 4, 1, 4, 1, 65, 0.25, 1, None, 0, None) == -2
+    # split-K needed but no workspace
+    assert LIB.kvc_paged_decode_attention(byref, 1, 1, 4, 1, 400, 1, 6400, 0.25, 1, None, 0,
+                                          None) == -5
+    # null q
+    assert LIB.kvc_paged_decode_attention(byref, None, 1, 4, 1, 4, 1, 64, 0.25, 1, None, 0,
+                                          None) == -1
+    assert LIB.kvc_kv_append(byref, 1, 1, 1, -1, None) == -2
+    assert LIB.kvc_kv_append(byref, None, 1, 1, 3, None) == -1
+    assert LIB.kvc_slot_mapping(1, 1, 4, 8, 1, 1, 5, 8, 1, None, None) == -4
+    assert LIB.kvc_slot_mapping(None, 1, 4, 8, 1, 1, 5, 16, 1, None, None) == -1
+    assert LIB.kvc_slot_mapping(1, 1, 4, 8, 1, 1, -5, 16, 1, None, None) == -2
+
+
+def test_zero_sized_calls_launch_nothing():
+    c = _cache()
+    assert LIB.kvc_kv_append(ctypes.byref(c), 1, 1, 1, 0, None) == 0
+    assert LIB.kvc_paged_decode_attention(ctypes.byref(c), 1, 0, 4, 1, 4, 1, 64, 0.25, 1, None,
+                                          0, None) == 0
+    assert LIB.kvc_slot_mapping(1, 1, 4, 8, 1, 1, 0, 16, 1, None, None) == 0
+
+
+def test_status_strings():
+    for s in range(-6, 1):
+        assert LIB.kvc_status_string(s)
+    assert LIB.kvc_status_string(-99) == b"unknown status"
