@@ -76,10 +76,15 @@ __global__ void chunk_append_kernel(uint8_t* __restrict__ kc, uint8_t* __restric
                                     const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
                                     const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
                                     const int32_t* __restrict__ block_table, int32_t max_blocks,
-                                    int32_t num_blocks, int32_t hkv, int32_t nc, int32_t* err) {
+                                    int32_t num_blocks, int32_t hkv, int32_t nc, int32_t total,
+                                    int32_t max_chunk, int32_t* err) {
   const int s = blockIdx.y;
   const int32_t t0 = cu[s], C = cu[s + 1] - t0, p0 = prefix[s];
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (!chunk_ok(t0, C, p0, total, max_chunk)) {
+    if (i == 0) flag_error(err, KVC_DEVERR_CONTEXT);
+    return;
+  }
   if (i >= (int64_t)C * hkv * nc) return;
   const int64_t row = i / nc;
   const int32_t c = (int32_t)(i - row * nc);
@@ -104,7 +109,7 @@ __global__ void chunk_append_kernel(uint8_t* __restrict__ kc, uint8_t* __restric
 }
 
 int launch_chunk_append(const kvc_cache* c, const void* k, const void* v, int32_t n_seqs,
-                        const int32_t* cu, const int32_t* prefix, int32_t max_chunk,
+                        const int32_t* cu, const int32_t* prefix, int32_t total, int32_t max_chunk,
                         const int32_t* block_table, int32_t max_blocks, hipStream_t st) {
   const int nc = c->head_dim * dtype_bytes(c->dtype) / 16;
   const int64_t per_seq = (int64_t)max_chunk * c->num_kv_heads * nc;
@@ -112,7 +117,8 @@ int launch_chunk_append(const kvc_cache* c, const void* k, const void* v, int32_
   dim3 grid((unsigned)ceil_div(per_seq, 256), (unsigned)n_seqs);
   hipLaunchKernelGGL(chunk_append_kernel, grid, dim3(256), 0, st, (uint8_t*)c->k_cache,
                      (uint8_t*)c->v_cache, (const uint8_t*)k, (const uint8_t*)v, cu, prefix,
-                     block_table, max_blocks, c->num_blocks, c->num_kv_heads, nc, c->err_flag);
+                     block_table, max_blocks, c->num_blocks, c->num_kv_heads, nc, total, max_chunk,
+                     c->err_flag);
   return launch_status();
 }
 

@@ -82,6 +82,8 @@ struct PrefillArgs {
   int32_t hkv;
   int32_t num_blocks;
   int32_t max_blocks;
+  int32_t total;
+  int32_t max_chunk;
   float scale_log2;
 };
 
@@ -114,6 +116,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_attention_kernel(Prefil
   const int C = a.cu[s + 1] - t0;
   const int p0 = a.prefix[s];
   const int pos_lo = qt * S::MP;
+  if (!chunk_ok(t0, C, p0, a.total, a.max_chunk)) {
+    if (qt == 0 && kvh == 0 && tid == 0) flag_error(a.err, KVC_DEVERR_CONTEXT);
+    return;
+  }
   if (pos_lo >= C) return;
   const int kv_len = p0 + C;                           // keys that exist after the write
   const int last_pos = p0 + min(pos_lo + S::MP, C) - 1;
@@ -159,7 +165,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_attention_kernel(Prefil
   auto row_off = [&](int key) -> int64_t {
     if (key >= kv_len) return -1;
     const int lb = key >> 4;
-    if (lb >= a.max_blocks) return -1;
+    if (lb >= a.max_blocks) {
+      flag_error(a.err, KVC_DEVERR_CONTEXT);
+      return -1;
+    }
     const int blk = bt_row[lb];
     if ((unsigned)blk >= (unsigned)a.num_blocks) {
       flag_error(a.err, KVC_DEVERR_BLOCK_ID);
@@ -387,8 +396,8 @@ extern "C" int kvc_chunked_prefill_attention(const kvc_cache* cache, const void*
   if (n_seqs == 0 || total_tokens == 0 || max_chunk_len == 0) return KVC_OK;
   if (!q || !k || !v || !cu_chunk_lens || !prefix_lens || !block_table || !out) return KVC_ERR_NULL;
   hipStream_t s = kvc::as_stream(stream);
-  st = kvc::launch_chunk_append(cache, k, v, n_seqs, cu_chunk_lens, prefix_lens, max_chunk_len,
-                                block_table, max_blocks, s);
+  st = kvc::launch_chunk_append(cache, k, v, n_seqs, cu_chunk_lens, prefix_lens, total_tokens,
+                                max_chunk_len, block_table, max_blocks, s);
   if (st != KVC_OK) return st;
   kvc::PrefillArgs a;
   a.q = q;
@@ -402,6 +411,8 @@ extern "C" int kvc_chunked_prefill_attention(const kvc_cache* cache, const void*
   a.hkv = cache->num_kv_heads;
   a.num_blocks = cache->num_blocks;
   a.max_blocks = max_blocks;
+  a.total = total_tokens;
+  a.max_chunk = max_chunk_len;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   return kvc::dispatch_prefill(a, cache->dtype, cache->head_dim, G, n_seqs, max_chunk_len, s);
 }

@@ -157,3 +157,74 @@ def max_rel(a, b):
 
 def default_scale(d):
     return 1.0 / math.sqrt(d)
+
+
+class PrefillCase:
+    """Chunked prefill for a batch of sequences: sequence i already holds
+    prefix[i] cached tokens and now writes + attends a chunk of chunk[i] tokens."""
+
+    def __init__(self, w: W.Workload, prefix, chunk, num_blocks: int, seed_extra: int = 0):
+        self.w = w
+        self.prefix = np.asarray(prefix, dtype=np.int64)
+        self.chunk = np.asarray(chunk, dtype=np.int64)
+        self.n = len(self.prefix)
+        self.total = self.prefix + self.chunk
+        self.num_blocks = num_blocks
+        self.bt = W.block_tables(w, self.total, num_blocks, seed_extra=seed_extra)
+        self.k, self.v, self.q = [], [], []
+        for i in range(self.n):
+            k, v, q = W.sequence_values(w, i, int(self.total[i]), int(self.chunk[i]))
+            self.k.append(k)
+            self.v.append(v)
+            self.q.append(q)
+
+    def oracle_rows(self, i: int, rows=None) -> np.ndarray:
+        dt = self.w.dtype
+        q = oracle_values(self.q[i], dt)
+        k = oracle_values(self.k[i], dt)
+        v = oracle_values(self.v[i], dt)
+        scale = OA.default_scale(self.w.D)
+        p0 = int(self.prefix[i])
+        if rows is None:
+            return OA.prefill_chunk_rows(q, k, v, p0, scale)
+        return np.stack([OA.attend_row(q[r], k[:p0 + r + 1], v[:p0 + r + 1], scale) for r in rows])
+
+    def oracle_pool(self):
+        bits = 16 if self.w.dtype == "bf16" else 32
+        pk = OP.empty_pool(self.num_blocks, self.w.Hkv, W.BLOCK_SIZE, self.w.D, bits)
+        pv = pk.copy()
+        for i in range(self.n):
+            n = int(self.total[i])
+            slots = OP.slots_for_positions(self.bt, [i] * n, np.arange(n), W.BLOCK_SIZE)
+            OP.scatter(pk, slots, oracle_bits(self.k[i], self.w.dtype))
+            OP.scatter(pv, slots, oracle_bits(self.v[i], self.w.dtype))
+        return pk, pv
+
+    def run_gpu(self, kvc, cache=None):
+        """Cache the prefixes through slot_mapping + kv_append, then one chunked
+        prefill call for all sequences. Returns (cache, out [sum C, Hq, D])."""
+        w, dev = self.w, "cuda"
+        if cache is None:
+            cache = kvc.PagedKVCache.allocate(self.num_blocks, w.Hkv, w.D, TDTYPE[w.dtype],
+                                              fill_bits=FILL)
+        bt = torch.from_numpy(self.bt).to(dev)
+        old = [i for i in range(self.n) if self.prefix[i] > 0]
+        if old:
+            seq = torch.from_numpy(np.concatenate(
+                [np.full(int(self.prefix[i]), i, np.int32) for i in old])).to(dev)
+            pos = torch.from_numpy(np.concatenate(
+                [np.arange(int(self.prefix[i]), dtype=np.int32) for i in old])).to(dev)
+            kk = to_device(np.concatenate([self.k[i][:self.prefix[i]] for i in old]), w.dtype)
+            vv = to_device(np.concatenate([self.v[i][:self.prefix[i]] for i in old]), w.dtype)
+            s = kvc.slot_mapping(bt, self.num_blocks, seq, pos, err_flag=cache.err_flag)
+            kvc.kv_append(cache, s, kk, vv)
+        cu = np.concatenate([[0], np.cumsum(self.chunk)]).astype(np.int32)
+        q = to_device(np.concatenate(self.q), w.dtype)
+        k = to_device(np.concatenate([self.k[i][self.prefix[i]:] for i in range(self.n)]), w.dtype)
+        v = to_device(np.concatenate([self.v[i][self.prefix[i]:] for i in range(self.n)]), w.dtype)
+        out = kvc.chunked_prefill_attention(
+            cache, q, k, v, torch.from_numpy(cu).to(dev),
+            torch.from_numpy(self.prefix.astype(np.int32)).to(dev), bt, int(self.chunk.max()))
+        torch.cuda.synchronize()
+        self.cu = cu
+        return cache, out

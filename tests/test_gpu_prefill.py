@@ -1,0 +1,118 @@
+"""GPU parity: chunked-prefill attention (MFMA) and its chunk K/V write."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests.gpu_cases import PrefillCase, assert_close, device_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kvc():
+    import kv_cache_decode_append_amd as m
+    return m
+
+
+def _check(kvc, case: PrefillCase, what: str, pool=True, rows=None):
+    cache, out = case.run_gpu(kvc)
+    assert int(cache.err_flag.item()) == 0
+    if pool:
+        pk, pv = case.oracle_pool()
+        assert np.array_equal(device_bits(cache.k_cache), pk), f"{what}: K pool differs"
+        assert np.array_equal(device_bits(cache.v_cache), pv), f"{what}: V pool differs"
+    got = out.float().cpu().numpy()
+    for i in range(case.n):
+        g = got[case.cu[i]:case.cu[i + 1]]
+        if rows is None:
+            assert_close(g, case.oracle_rows(i), case.w.dtype, f"{what} seq {i}")
+        else:
+            r = rows(i)
+            assert_close(g[r], case.oracle_rows(i, r), case.w.dtype, f"{what} seq {i}")
+    return cache, out
+
+
+def test_c1_prompt_prefill(kvc):
+    """C1's 16-token prompt (prefix 0), fp32, MHA 4/4, head_dim 16."""
+    say("prefill C1 prompt fp32")
+    case = PrefillCase(W.C1, [0], [W.C1_PROMPT], W.C1_POOL_BLOCKS)
+    _check(kvc, case, "C1 prefill")
+
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+@pytest.mark.parametrize("dtype,d", [("fp32", 16), ("fp32", 64), ("fp32", 128), ("bf16", 32),
+                                     ("bf16", 64), ("bf16", 128)])
+def test_ragged_batch(kvc, dtype, d, g):
+    say(f"prefill ragged batch {dtype} D={d} G={g}")
+    w = W.small_workload(f"pf-{dtype}-{d}-{g}", 900 + g * 1000 + d, B=6, Hq=2 * g, Hkv=2, D=d,
+                         dtype=dtype, sigma=0.5 if dtype == "bf16" else 1.0)
+    prefix = [0, 17, 100, 31, 64, 0]
+    chunk = [1, 16, 33, 200, 64, 130]
+    case = PrefillCase(w, prefix, chunk, 120)
+    _check(kvc, case, f"{dtype} D={d} G={g}")
+
+
+def test_chunked_equals_one_shot_bf16(kvc):
+    """Prefill in chunks [0,100), [100,257), [257,300) gives the same cache bits
+    and, within tolerance, the same rows as one 300-token prefill."""
+    say("prefill chunked vs one-shot bf16 32/8/128")
+    w = W.small_workload("pf-chunks", 950, B=1, Hq=32, Hkv=8, D=128, dtype="bf16", sigma=0.5)
+    one = PrefillCase(w, [0], [300], 40)
+    c1, o1 = one.run_gpu(kvc)
+    ref = one.oracle_rows(0)
+    assert_close(o1.float().cpu().numpy(), ref, "bf16", "one-shot")
+    cache = kvc.PagedKVCache.allocate(40, w.Hkv, w.D, torch.bfloat16, fill_bits=-1)
+    outs = []
+    from tests.gpu_cases import to_device
+    dev = "cuda"
+    for a, b in [(0, 100), (100, 257), (257, 300)]:
+        # each call writes only its chunk; earlier chunks are already cached
+        cu = torch.tensor([0, b - a], dtype=torch.int32, device=dev)
+        out = kvc.chunked_prefill_attention(
+            cache, to_device(one.q[0][a:b], "bf16"), to_device(one.k[0][a:b], "bf16"),
+            to_device(one.v[0][a:b], "bf16"), cu, torch.tensor([a], dtype=torch.int32, device=dev),
+            torch.from_numpy(one.bt).to(dev), b - a)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(cache.k_cache.view(torch.int16), c1.k_cache.view(torch.int16))
+    assert torch.equal(cache.v_cache.view(torch.int16), c1.v_cache.view(torch.int16))
+    assert_close(torch.cat(outs).float().cpu().numpy(), ref, "bf16", "chunked")
+
+
+def test_one_token_chunk_matches_decode(kvc):
+    say("prefill with C = 1 vs decode of the same position")
+    w = W.small_workload("pf-c1", 960, B=3, Hq=32, Hkv=8, D=128, dtype="bf16", sigma=0.5)
+    case = PrefillCase(w, [2100, 15, 0], [1, 1, 1], 200)
+    cache, out = case.run_gpu(kvc)
+    bt = torch.from_numpy(case.bt).cuda()
+    ctx = torch.from_numpy(case.total.astype(np.int32)).cuda()
+    from tests.gpu_cases import to_device
+    dec = kvc.paged_decode_attention(cache, to_device(np.concatenate(case.q), "bf16"), bt, ctx,
+                                     int(case.total.max()))
+    torch.cuda.synchronize()
+    ref = np.concatenate([case.oracle_rows(i) for i in range(3)])
+    assert_close(out.float().cpu().numpy(), ref, "bf16", "prefill C=1")
+    assert_close(dec.float().cpu().numpy(), ref, "bf16", "decode")
+
+
+def test_c5_prefill_chunk_over_long_prefix(kvc):
+    """C5: 8 sequences x a 2,048-token chunk over a 30,000-token cached prefix.
+    Rows sampled per sequence (first, last, block edges and seeded random)."""
+    say("prefill C5: 8 x 2048 over 30,000 prefix, bf16, sampled rows")
+    n = W.C5.B
+    case = PrefillCase(W.C5, [W.C5_PREFIX] * n, [W.C5_CHUNK] * n,
+                       n * W.blocks_for(W.C5_PREFIX + W.C5_CHUNK))
+    rng = np.random.default_rng(961)
+
+    def rows(i):
+        return sorted(set([0, 1, 15, 16, 1023, 2047] + rng.integers(0, W.C5_CHUNK, 4).tolist()))
+    cache, _ = _check(kvc, case, "C5 prefill", pool=False, rows=rows)
+    # the chunk's K/V landed at their slots (sampled tokens, bitwise)
+    from oracle import paged as OP
+    from tests.gpu_cases import oracle_bits
+    kb = device_bits(cache.k_cache)
+    for i in range(n):
+        for p in [W.C5_PREFIX, W.C5_PREFIX + 1, W.C5_PREFIX + 2047]:
+            s = OP.slot_of(case.bt[i], p, 16)
+            assert np.array_equal(kb[s // 16, :, s % 16, :], oracle_bits(case.k[i][p], "bf16"))
