@@ -5,15 +5,22 @@ Workload (Llama-3.1-8B attention shape, batch 64, context ~2k): 32 query heads,
 in [2000, 2300] counting the new token, one 9,200-block pool per layer for 32
 layers (17.97 GiB of K/V in HBM, so repeated steps cannot be served from the
 256 MB Infinity Cache). A step is one decode step of the whole model's
-attention: slot mapping of the 64 new tokens, then for each of the 32 layers
-kv_append of the new K/V and paged decode attention (with its split-K merge).
+attention: for each of the 32 layers one fused launch that computes the 64 new
+tokens' slots, appends their K/V to the paged cache and runs paged decode
+attention (split-K merge pass only when a sequence spans several partitions).
 Inputs are synthetic and resident in HBM before the timed region.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--workload c3-decode|c5-decode|c5-prefill]
+
+The default workload is the one above (c3-decode). c5-decode (8 sequences at
+32,000 tokens, split-K) and c5-prefill (8 x a 2,048-token chunk over a
+30,000-token cached prefix, MFMA) measure the other kernels of the path on the
+long-context workload; each prints its own line with its own roofline.
 
 Prints ONE JSON line. `value` is KV bytes read per second over the whole step.
-The `roofline` entry is for the decode-attention call (paged_decode_kernel +
-decode_merge_kernel), timed with HIP events on the stream it runs on.
+The `roofline` entry is for the per-layer decode launch (paged_decode_kernel,
+with the append fused in), timed with HIP events on the stream it runs on.
 """
 from __future__ import annotations
 
@@ -38,6 +45,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--workload", default="c3-decode",
+                    choices=["c3-decode", "c5-decode", "c5-prefill"])
     return ap.parse_args()
 
 
@@ -98,6 +107,11 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "c5-decode":
+        return bench_c5_decode(args)
+    if args.workload == "c5-prefill":
+        return bench_c5_prefill(args)
+
     import torch
 
     import kv_cache_decode_append_amd as kvc
@@ -136,21 +150,16 @@ def main():
     out = [torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev) for _ in range(L)]
     bt = torch.from_numpy(bt_np).to(dev)
     ctx = torch.from_numpy(ctx_np.astype(np.int32)).to(dev)
-    seq_ids = torch.arange(B, dtype=torch.int32, device=dev)
-    pos = (ctx - 1).to(torch.int32)
-    slots = torch.empty(B, dtype=torch.int64, device=dev)
     ws = torch.empty(max(1, kvc.decode_workspace_bytes(B, Hq, D, max_ctx)), dtype=torch.uint8,
                      device=dev)
     torch.cuda.synchronize()
 
     def step(ev=None):
-        kvc.slot_mapping(bt, nb, seq_ids, pos, out=slots)
         for layer in range(L):
-            kvc.kv_append(caches[layer], slots, kn[layer], vn[layer])
             if ev is not None:
                 ev[layer][0].record()
-            kvc.paged_decode_attention(caches[layer], q[layer], bt, ctx, max_ctx,
-                                       out=out[layer], workspace=ws)
+            kvc.decode_append_attention(caches[layer], q[layer], kn[layer], vn[layer], bt, ctx,
+                                        max_ctx, out=out[layer], workspace=ws)
             if ev is not None:
                 ev[layer][1].record()
 
@@ -162,22 +171,27 @@ def main():
         print(f"bench sanity check failed: err flags {errs}", file=sys.stderr)
         sys.exit(1)
 
-    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-               for _ in range(L)] for _ in range(args.steps)]
+    # Per-layer kernel events are recorded in every EVERY-th timed step only,
+    # so that their own cost barely touches ms_per_step.
+    EVERY = 5
+    timed = [s for s in range(args.steps) if s % EVERY == 0]
+    events = {s: [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+                  for _ in range(L)] for s in timed}
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for s in range(args.steps):
-        step(events[s])
+        step(events.get(s))
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    dec_ms = np.array([[e[0].elapsed_time(e[1]) for e in st] for st in events])
+    dec_ms = np.array([[e[0].elapsed_time(e[1]) for e in events[s]] for s in timed])
 
     kv_bytes_layer = int(ctx_np.sum()) * Hkv * D * 2 * 2
     io_bytes_layer = (B * Hq * D * 2 * 2            # q in, out
+                      + B * Hkv * D * 2 * 2 * 2     # new K/V read and written to the cache
                       + B * bt_np.shape[1] * 4 + B * 4)   # block table, context lengths
     kv_gbs = kv_bytes_layer * L / (ms_per_step * 1e-3) / 1e9
     dec_avg_us = float(dec_ms.mean() * 1e3)
@@ -208,7 +222,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_kernel + decode_merge_kernel (one decode-attention call)",
+            "kernel": "paged_decode_kernel (fused append + decode attention, one launch per layer)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -221,6 +235,115 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_budget_s)
+    print(json.dumps(res), flush=True)
+
+
+def _timed(fn, steps, warmup):
+    """Mean milliseconds per call over `steps` calls, HIP events on torch's stream."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(steps):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def _base_line(args, metric, value, unit, ms, dtype, config, roofline):
+    return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "accumulate": "fp32",
+            "data": "synthetic", "config": config, "roofline": roofline, "cpu_baseline": None}
+
+
+def bench_c5_decode(args):
+    """8 sequences x 32,000 tokens, GQA 32/8/128 bf16, fused append + split-K decode.
+    Eight layer pools (2.1 GB each) are rotated so the Infinity Cache cannot hold them."""
+    import torch
+
+    import kv_cache_decode_append_amd as kvc
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = W.C5
+    B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
+    ctx_np = W.context_lengths(w)
+    nb = B * W.blocks_for(W.C5_CTX)
+    bt = torch.from_numpy(W.block_tables(w, ctx_np, nb)).to(dev)
+    ctx = torch.from_numpy(ctx_np.astype(np.int32)).to(dev)
+    L = 8
+    caches = []
+    for _ in range(L):
+        c = kvc.PagedKVCache.allocate(nb, Hkv, D, torch.bfloat16, device=dev)
+        c.k_cache.normal_(0, 0.5)
+        c.v_cache.normal_(0, 0.5)
+        caches.append(c)
+    q = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
+    kn = torch.empty(B, Hkv, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
+    vn = torch.empty_like(kn)
+    out = torch.empty_like(q)
+    ws = torch.empty(kvc.decode_workspace_bytes(B, Hq, D, W.C5_CTX), dtype=torch.uint8, device=dev)
+    ms = _timed(lambda i: kvc.decode_append_attention(caches[i % L], q, kn, vn, bt, ctx, W.C5_CTX,
+                                                      out=out, workspace=ws),
+                args.steps, args.warmup)
+    kv = int(ctx_np.sum()) * Hkv * D * 2 * 2
+    gbs = kv / (ms * 1e-3) / 1e9
+    res = _base_line(args, "long-context decode KV-read GB/s, B=8 ctx 32k", round(gbs, 1), "GB/s",
+                     ms, "bf16",
+                     {"workload": "decode B=8 ctx 32,000, GQA 32/8, head_dim 128, bf16 paged cache, "
+                                  "split-K + merge", "B": B, "ctx": W.C5_CTX},
+                     {"bound": "hbm", "kernel": "paged_decode_kernel + decode_merge_kernel",
+                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                      "avg_us": round(ms * 1e3, 2), "bytes_per_launch": kv})
+    print(json.dumps(res), flush=True)
+
+
+def bench_c5_prefill(args):
+    """8 sequences, each a 2,048-token chunk over a 30,000-token cached prefix
+    (chunk K/V write + causal attention on MFMA). Algorithmic work counts only
+    unmasked (query, key) pairs at 4 * head_dim flop each."""
+    import torch
+
+    import kv_cache_decode_append_amd as kvc
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = W.C5
+    n, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
+    P, C = W.C5_PREFIX, W.C5_CHUNK
+    total = np.full(n, P + C)
+    nb = n * W.blocks_for(P + C)
+    bt = torch.from_numpy(W.block_tables(w, total, nb)).to(dev)
+    cache = kvc.PagedKVCache.allocate(nb, Hkv, D, torch.bfloat16, device=dev)
+    cache.k_cache.normal_(0, 0.5)
+    cache.v_cache.normal_(0, 0.5)
+    q = torch.empty(n * C, Hq, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
+    k = torch.empty(n * C, Hkv, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
+    v = torch.empty_like(k)
+    out = torch.empty_like(q)
+    cu = torch.arange(0, (n + 1) * C, C, dtype=torch.int32, device=dev)
+    pre = torch.full((n,), P, dtype=torch.int32, device=dev)
+    steps = max(1, args.steps // 10)
+    ms = _timed(lambda i: kvc.chunked_prefill_attention(cache, q, k, v, cu, pre, bt, C, out=out),
+                steps, max(1, args.warmup // 10))
+    pairs = n * Hq * (C * P + C * (C + 1) // 2)
+    flop = pairs * 4 * D
+    tf = flop / (ms * 1e-3) / 1e12
+    res = _base_line(args, "chunked-prefill attention TFLOP/s, 8 x 2,048 over a 30,000 prefix",
+                     round(tf, 1), "TFLOP/s", ms, "bf16",
+                     {"workload": "chunked prefill, 8 sequences x 2,048-token chunk over a "
+                                  "30,000-token cached prefix, GQA 32/8, head_dim 128, bf16",
+                      "n_seqs": n, "chunk": C, "prefix": P},
+                     {"bound": "mfma", "kernel": "chunk_append_kernel + prefill_attention_kernel",
+                      "achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                      "frac": round(tf / 2500.0, 4), "traffic": None,
+                      "avg_us": round(ms * 1e3, 1), "flop_per_launch": flop})
+    res["steps"] = steps
     print(json.dumps(res), flush=True)
 
 

@@ -141,6 +141,21 @@ int kvc_paged_decode_attention(const kvc_cache* cache, const void* q, int32_t B,
                                float softmax_scale, void* out, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* One decode step in one launch: for every sequence b with context_lens[b] >= 1,
+ * write k_new[b], v_new[b] ([num_kv_heads][head_dim], cache dtype) at position
+ * context_lens[b] - 1 through the block table (append first), then attend q[b]
+ * over positions 0 .. context_lens[b] - 1 (aiwithghost.com, section "What does a
+ * KV cache keep?": compute the new token's K/V/Q, append, attend over everything
+ * stored). Same arguments, outputs and workspace rule as
+ * kvc_paged_decode_attention; the cache and `out` end up bit-identical to
+ * kvc_slot_mapping + kvc_kv_append + kvc_paged_decode_attention. */
+int kvc_decode_append_attention(const kvc_cache* cache, const void* q, const void* k_new,
+                                const void* v_new, int32_t B, int32_t Hq,
+                                const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* context_lens, int32_t max_context_len,
+                                float softmax_scale, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Chunked prefill: write a prompt chunk's K/V into the cache, then causal
  * attention of each chunk position over the cached prefix plus the chunk's
  * positions up to and including itself.

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     KvcError,
     PagedKVCache,
     chunked_prefill_attention,
+    decode_append_attention,
     decode_workspace_bytes,
     kv_append,
     kv_bytes_per_token,

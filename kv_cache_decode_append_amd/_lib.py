@@ -57,7 +57,7 @@ def _hip_runtimes_mapped() -> set[str]:
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m kv_cache_decode_append_amd.build`")
+                          "`python kv_cache_decode_append_amd/build.py`")
     # torch's own HIP runtime must already be mapped so that the library binds
     # to it (same soname) instead of loading a second runtime.
     import torch.cuda  # noqa: F401
@@ -75,6 +75,8 @@ def _load() -> ctypes.CDLL:
         "kvc_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32]),
         "kvc_paged_decode_attention": (c_int, [P, vp, c_i32, c_i32, vp, c_i32, vp, c_i32, fl, vp,
                                                vp, c_sz, vp]),
+        "kvc_decode_append_attention": (c_int, [P, vp, vp, vp, c_i32, c_i32, vp, c_i32, vp, c_i32,
+                                                fl, vp, vp, c_sz, vp]),
         "kvc_chunked_prefill_attention": (c_int, [P, vp, vp, vp, c_i32, vp, vp, c_i32, c_i32, vp,
                                                   c_i32, c_i32, fl, vp, vp]),
         "kvc_status_string": (ctypes.c_char_p, [c_int]),
@@ -200,10 +202,8 @@ def decode_workspace_bytes(B: int, Hq: int, head_dim: int, max_context_len: int)
     return int(LIB.kvc_decode_workspace_bytes(B, Hq, head_dim, max_context_len))
 
 
-def paged_decode_attention(cache: PagedKVCache, q: torch.Tensor, block_table: torch.Tensor,
-                           context_lens: torch.Tensor, max_context_len: int,
-                           softmax_scale: float | None = None, out: torch.Tensor | None = None,
-                           workspace: torch.Tensor | None = None) -> torch.Tensor:
+def _decode(cache, q, k_new, v_new, block_table, context_lens, max_context_len, softmax_scale,
+            out, workspace):
     dev = cache.k_cache.device
     _need(q, "q", cache.dtype, 3, dev)
     _need(block_table, "block_table", torch.int32, 2, dev)
@@ -211,6 +211,11 @@ def paged_decode_attention(cache: PagedKVCache, q: torch.Tensor, block_table: to
     B, Hq, D = q.shape
     if D != cache.head_dim or block_table.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("q / block_table / context_lens shapes disagree")
+    if k_new is not None:
+        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+            _need(t, n, cache.dtype, 3, dev)
+            if t.shape != (B, cache.num_kv_heads, D):
+                raise ValueError(f"{n} must be [{B}, {cache.num_kv_heads}, {D}]")
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", cache.dtype, 3, dev)
@@ -223,11 +228,36 @@ def paged_decode_attention(cache: PagedKVCache, q: torch.Tensor, block_table: to
     if workspace is not None:
         _need(workspace, "workspace", device=dev)
     scale = (1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
-    _check("kvc_paged_decode_attention", LIB.kvc_paged_decode_attention(
-        cache.c, q.data_ptr(), B, Hq, block_table.data_ptr(), block_table.shape[1],
-        context_lens.data_ptr(), int(max_context_len), scale, out.data_ptr(),
-        _ptr(workspace), ws_bytes, _stream()))
+    if k_new is None:
+        _check("kvc_paged_decode_attention", LIB.kvc_paged_decode_attention(
+            cache.c, q.data_ptr(), B, Hq, block_table.data_ptr(), block_table.shape[1],
+            context_lens.data_ptr(), int(max_context_len), scale, out.data_ptr(),
+            _ptr(workspace), ws_bytes, _stream()))
+    else:
+        _check("kvc_decode_append_attention", LIB.kvc_decode_append_attention(
+            cache.c, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), B, Hq,
+            block_table.data_ptr(), block_table.shape[1], context_lens.data_ptr(),
+            int(max_context_len), scale, out.data_ptr(), _ptr(workspace), ws_bytes, _stream()))
     return out
+
+
+def paged_decode_attention(cache: PagedKVCache, q: torch.Tensor, block_table: torch.Tensor,
+                           context_lens: torch.Tensor, max_context_len: int,
+                           softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Attend each q[b] over positions 0 .. context_lens[b]-1 of its cached K/V."""
+    return _decode(cache, q, None, None, block_table, context_lens, max_context_len,
+                   softmax_scale, out, workspace)
+
+
+def decode_append_attention(cache: PagedKVCache, q: torch.Tensor, k_new: torch.Tensor,
+                            v_new: torch.Tensor, block_table: torch.Tensor,
+                            context_lens: torch.Tensor, max_context_len: int,
+                            softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """One fused decode step: append k_new/v_new at position context_lens[b]-1, then attend."""
+    return _decode(cache, q, k_new, v_new, block_table, context_lens, max_context_len,
+                   softmax_scale, out, workspace)
 
 
 def chunked_prefill_attention(cache: PagedKVCache, q: torch.Tensor, k: torch.Tensor,

@@ -1,6 +1,8 @@
 """Build libkvc.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
 
-    python -m kv_cache_decode_append_amd.build [--jobs N]
+    python kv_cache_decode_append_amd/build.py [--jobs N]
+
+(run by path, not with -m: importing the package loads the library it builds)
 
 Every .hip / .cpp file under csrc/ is compiled to an object with hipcc and the
 objects are linked into kv_cache_decode_append_amd/libkvc.so. Packed-fp32 VALU

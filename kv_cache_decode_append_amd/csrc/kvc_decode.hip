@@ -35,6 +35,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "kvc_device.h"
 #include "kvc_host.h"
 
@@ -42,6 +44,7 @@ namespace kvc {
 
 constexpr int kWaves = 4;
 constexpr int kMinPartBlocks = 16;
+constexpr int kMaxPartBlocks = kWaves * 64;   // one block id per lane of each wave
 
 template <typename T, int D, int G>
 struct DecodeShape {
@@ -50,20 +53,29 @@ struct DecodeShape {
   static constexpr int NC = RB / 16;            // 16-byte chunks per row
   static constexpr int CE = 16 / EB;            // elements per chunk
   static constexpr int TILE = 16 * RB;          // one (block, kv head) tile, bytes
-  static constexpr int LPH = (G == 8) ? 8 : 16; // QK lanes per query head
-  static constexpr int SPL = 16 / LPH;          // tokens per QK lane per block
+  static constexpr int QS = 2;                  // lanes sharing one (head, token) dot product
+  static constexpr int NCQ = NC / QS;           // query chunks held per lane
+  static constexpr int LPH = (G == 8) ? 8 : 16; // QK lanes per query head (one DPP row or half)
+  static constexpr int TPS = LPH / QS;          // tokens per QK sub-step
+  static constexpr int SPL = 16 / TPS;          // QK sub-steps per block
   static constexpr int TPI = 64 / NC;           // V tokens covered by one wave load
   static constexpr int NI = NC / 4;             // 16-byte loads per lane per tile
+  // bf16 PV on v_dot2_f32_bf16: a lane holds NI tokens of the same dims, paired up
+  static constexpr bool DOT2_PV = (EB == 2) && (NI >= 2);
+  // blocks in flight per wave (register ring)
+  static constexpr int PF = (EB == 2 && G <= 4 && D <= 128) ? 3 : 2;
   static constexpr int KST = kWaves * TILE;     // K staging, all waves
   static constexpr int RED = kWaves * TPI * G * D * 4;   // end-of-kernel reduction
   static constexpr int AREA = KST > RED ? KST : RED;
   static constexpr int SMEM = AREA + kWaves * 16 * G * 4 + kWaves * G * 8;
-  static_assert(NC >= 4 && NC <= 64, "row of 64..1024 bytes");
+  static_assert(NC >= 4 && NC <= 32, "row of 64..512 bytes");
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "G in {1,2,4,8}");
 };
 
 struct DecodeArgs {
   const void* q;
+  const void* k_new;  // fused append: [B][hkv][D] new K/V at position ctx-1, or null
+  const void* v_new;
   const void* kc;
   const void* vc;
   const int32_t* bt;
@@ -143,7 +155,10 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
 
   const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform across the wave; saying so keeps every buffer
+  // descriptor and loop bound in scalar registers (no per-lane waterfall)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hq_all = a.hkv * G;
 
   const int ctx = effective_ctx(a, b, part == 0 && kvh == 0 && tid == 0);
@@ -161,30 +176,39 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
 
   uint8_t* kst = smem + w * S::TILE;
   float* plds = reinterpret_cast<float*>(smem + S::AREA) + w * 16 * G;
+  uint16_t* p16 = reinterpret_cast<uint16_t*>(plds);          // bf16 weight pairs (DOT2_PV)
+  const uint32_t* p32 = reinterpret_cast<const uint32_t*>(plds);
   float2* ml = reinterpret_cast<float2*>(smem + S::AREA + kWaves * 16 * G * 4);
 
-  // QK layout: lane -> (head h, token slot tq)
-  const int h = lane / S::LPH, tq = lane % S::LPH;
+  // QK layout: lane -> (head h, token slot tt, half qh of the head dim). The two
+  // lanes of a pair (qh = 0, 1) hold the two halves of the query row and add
+  // their partial dot products with one DPP step.
+  const int h = lane / S::LPH, qh = (lane % S::LPH) % S::QS, tt = (lane % S::LPH) / S::QS;
   const bool active = h < G;
-  u32x4 qv[S::NC];
+  u32x4 qv[S::NCQ];
   {
     const int hq = kvh * G + (active ? h : 0);
     const u32x4* qp = reinterpret_cast<const u32x4*>(
         reinterpret_cast<const uint8_t*>(a.q) + ((size_t)b * hq_all + hq) * S::RB);
 #pragma unroll
-    for (int c = 0; c < S::NC; ++c) qv[c] = qp[c];
+    for (int c = 0; c < S::NCQ; ++c) qv[c] = qp[qh * S::NCQ + c];
   }
 
   const int32_t* bt_row = a.bt + (size_t)b * a.max_blocks;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kc);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vc);
 
+  // This wave's block ids, one per lane (a partition has at most 4 x 64 blocks):
+  // inside the loop they are picked with v_readlane, so no block-table load
+  // sits behind the prefetch ring in the in-order load counter.
+  const int32_t my_blk = lane < n_my ? bt_row[blk0 + w + lane * kWaves] : -1;
+
   // Issue the loads of this wave's i-th block into (kb, vb).
   auto issue = [&](u32x4 (&kb)[S::NI], u32x4 (&vb)[S::NI], int i) {
     size_t off = 0;
     uint32_t bytes = 0;
     if (i < n_my) {
-      int blk = __builtin_amdgcn_readfirstlane(bt_row[blk0 + w + i * kWaves]);
+      const int blk = __builtin_amdgcn_readlane(my_blk, i);
       if ((unsigned)blk < (unsigned)a.num_blocks) {
         off = ((size_t)blk * a.hkv + kvh) * S::TILE;
         bytes = S::TILE;
@@ -207,8 +231,37 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
 #pragma unroll
     for (int e = 0; e < S::CE; ++e) acc[hh][e] = 0.f;
 
-  auto process = [&](const u32x4 (&kb)[S::NI], const u32x4 (&vb)[S::NI], int i) {
+  // Fused append. Every load of a tile gives lane `lane` chunk (lane % NC) of
+  // some token, so each lane needs one 16-byte chunk of the new row; it is read
+  // here, before the pipelined loop (memory operations inside the loop would
+  // make the compiler wait on the whole prefetch ring), substituted in
+  // registers when the last block is processed, and stored to the cache after
+  // the loop. Only the workgroup whose partition holds the last block does so.
+  const bool fuse = a.k_new != nullptr && part == n_used - 1;
+  const int t_new = (ctx - 1) & 15;
+  u32x4 k_new_c = u32x4{0u, 0u, 0u, 0u}, v_new_c = u32x4{0u, 0u, 0u, 0u};
+  if (fuse) {
+    const size_t src = ((size_t)b * a.hkv + kvh) * S::RB + (lane % S::NC) * 16;
+    k_new_c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.k_new) + src);
+    v_new_c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.v_new) + src);
+  }
+  // One block. TAIL marks the sequence's last block, the only one that can be
+  // partial or hold the appended token; every other block skips the masking
+  // and substitution code entirely.
+  auto process = [&](auto tail_tag, u32x4 (&kb)[S::NI], u32x4 (&vb)[S::NI], int i) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
     const int lb = blk0 + w + i * kWaves;
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int j = 0; j < S::NI; ++j) {
+        const int tk = (j * 64 + lane) / S::NC;
+        if (fuse && tk == t_new) {
+          kb[j] = k_new_c;
+          vb[j] = v_new_c;
+        }
+        if (lb * 16 + tk >= ctx) vb[j] = u32x4{0u, 0u, 0u, 0u};   // unwritten rows may hold NaN
+      }
+    }
     // K tile -> LDS, chunk c of token t at chunk slot c ^ (t % NC)
 #pragma unroll
     for (int j = 0; j < S::NI; ++j) {
@@ -220,18 +273,22 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
     float s[S::SPL];
 #pragma unroll
     for (int sl = 0; sl < S::SPL; ++sl) {
-      const int t = tq + S::LPH * sl;
+      const int t = tt + S::TPS * sl;
       float part_s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < S::NC; ++c) {
+      for (int cc = 0; cc < S::NCQ; ++cc) {
+        const int c = qh * S::NCQ + cc;
         const u32x4 kk = *reinterpret_cast<const u32x4*>(kst + t * S::RB + ((c ^ (t % S::NC)) << 4));
-        chunk_dot<T>(kk, qv[c], part_s);
+        chunk_dot<T>(kk, qv[cc], part_s);
       }
-      const float sc = ((part_s[0] + part_s[1]) + (part_s[2] + part_s[3])) * a.scale_log2;
-      s[sl] = (active && lb * 16 + t < ctx) ? sc : -INFINITY;
+      float dot = (part_s[0] + part_s[1]) + (part_s[2] + part_s[3]);
+      dot += dpp_f<kQuadXor1>(dot);                  // the other half of the head dim
+      const bool valid = active && (!TAIL || lb * 16 + t < ctx);
+      s[sl] = valid ? dot * a.scale_log2 : -INFINITY;
     }
 
-    // online softmax over this block's tokens, per head
+    // online softmax over this block's tokens, per head (each token sits in
+    // both lanes of its pair: harmless for the max, counted once in the sum)
     float mx = s[0];
 #pragma unroll
     for (int sl = 1; sl < S::SPL; ++sl) mx = fmaxf(mx, s[sl]);
@@ -243,18 +300,32 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
 #pragma unroll
     for (int sl = 0; sl < S::SPL; ++sl) {
       p[sl] = __builtin_amdgcn_exp2f(s[sl] - m_safe);
-      ps += p[sl];
+      // bf16 PV multiplies by bf16 weights: round once here so that the
+      // normaliser l sums exactly the weights the numerator uses
+      if constexpr (S::DOT2_PV) p[sl] = __uint_as_float(f32_to_bf16_bits(p[sl]) << 16);
+      ps += (qh == 0) ? p[sl] : 0.f;
     }
     ps = group_sum<S::LPH>(ps);
     l_run = l_run * alpha + ps;
     m_run = m_new;
-    if (active) {
+    if (active && qh == 0) {
 #pragma unroll
-      for (int sl = 0; sl < S::SPL; ++sl) plds[(tq + S::LPH * sl) * G + h] = p[sl];
+      for (int sl = 0; sl < S::SPL; ++sl) {
+        const int t = tt + S::TPS * sl;
+        if constexpr (S::DOT2_PV) {
+          // packed bf16 pairs in PV order: token t = j*TPI + r sits in pair
+          // (j/2)*TPI + r, low half for even j
+          const int jt = t / S::TPI, r = t % S::TPI;
+          p16[((jt >> 1) * S::TPI + r) * (2 * G) + 2 * h + (jt & 1)] =
+              (uint16_t)(__float_as_uint(p[sl]) >> 16);
+        } else {
+          plds[t * G + h] = p[sl];
+        }
+      }
     }
     __builtin_amdgcn_wave_barrier();
 
-    // rescale the accumulators when a running max moved
+    // rescale the accumulators when a running max moved (rare after the first blocks)
     float al[G];
     bool moved = false;
 #pragma unroll
@@ -262,41 +333,93 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
       al[hh] = readlane_f(alpha, hh * S::LPH);
       moved |= (al[hh] != 1.f);
     }
-    if (moved) {
+    if (__builtin_expect(moved, 0)) {
 #pragma unroll
       for (int hh = 0; hh < G; ++hh)
 #pragma unroll
         for (int e = 0; e < S::CE; ++e) acc[hh][e] *= al[hh];
     }
 
-    // PV: lane owns chunk (lane % NC) of token j*TPI + lane / NC
-    const bool tail = (lb == nblk - 1) && ((ctx & 15) != 0);
+    // PV: lane owns chunk (lane % NC) of tokens j*TPI + lane / NC, j < NI
+    if constexpr (S::DOT2_PV) {
+      // tokens of loads (2m, 2m+1) form a pair; one v_dot2 per (head, dim) and pair
 #pragma unroll
-    for (int j = 0; j < S::NI; ++j) {
-      const int tv = j * S::TPI + lane / S::NC;
-      float pv[G];
+      for (int m = 0; m < S::NI / 2; ++m) {
+        const int pr = m * S::TPI + lane / S::NC;
+        const u32x4 va = vb[2 * m], vbb = vb[2 * m + 1];
+        uint32_t pp[G];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) pv[hh] = plds[tv * G + hh];
-      u32x4 vv = vb[j];
-      if (tail && lb * 16 + tv >= ctx) vv = u32x4{0u, 0u, 0u, 0u};   // unwritten rows may hold NaN
-      float x[S::CE];
-      unpack<T, S::CE>(vv, x);
+        for (int hh = 0; hh < G; ++hh) pp[hh] = p32[pr * G + hh];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh)
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t xlo = __builtin_amdgcn_perm(vbb[k], va[k], 0x05040100u);
+          const uint32_t xhi = __builtin_amdgcn_perm(vbb[k], va[k], 0x07060302u);
 #pragma unroll
-        for (int e = 0; e < S::CE; ++e) acc[hh][e] = fmaf(pv[hh], x[e], acc[hh][e]);
+          for (int hh = 0; hh < G; ++hh) {
+            acc[hh][2 * k] = dot2_bf16(pp[hh], xlo, acc[hh][2 * k]);
+            acc[hh][2 * k + 1] = dot2_bf16(pp[hh], xhi, acc[hh][2 * k + 1]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < S::NI; ++j) {
+        const int tv = j * S::TPI + lane / S::NC;
+        float pv[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) pv[hh] = plds[tv * G + hh];
+        float x[S::CE];
+        unpack<T, S::CE>(vb[j], x);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+          for (int e = 0; e < S::CE; ++e) acc[hh][e] = fmaf(pv[hh], x[e], acc[hh][e]);
+      }
     }
   };
 
   {
-    u32x4 kb0[S::NI], vb0[S::NI], kb1[S::NI], vb1[S::NI];
-    issue(kb0, vb0, 0);
-    issue(kb1, vb1, 1);
-    for (int i = 0; i < n_my; i += 2) {
-      process(kb0, vb0, i);
-      issue(kb0, vb0, i + 2);
-      if (i + 1 < n_my) process(kb1, vb1, i + 1);
-      issue(kb1, vb1, i + 3);
+    // Ring of PF blocks in flight; a slot is refilled right after it is used.
+    // A wave's blocks ascend, so only its last step can be the sequence's last
+    // block: the loop runs the plain path only and the last step is peeled.
+    u32x4 kb[S::PF][S::NI], vb[S::PF][S::NI];
+#pragma unroll
+    for (int u = 0; u < S::PF; ++u) issue(kb[u], vb[u], u);
+    const int n_main = n_my > 0 ? n_my - 1 : 0;
+    for (int i = 0; i < n_main; i += S::PF) {
+#pragma unroll
+      for (int u = 0; u < S::PF; ++u) {
+        if (i + u < n_main) {
+          process(std::false_type{}, kb[u], vb[u], i + u);
+          // keep the refill of this slot after its use: hoisting the loads
+          // above the PV products would force a register copy of the tile
+          __builtin_amdgcn_sched_barrier(0);
+          issue(kb[u], vb[u], i + u + S::PF);
+        }
+      }
+    }
+    if (n_my > 0) {
+      const int last = n_my - 1, slot = last % S::PF;
+      const bool tail = blk0 + w + last * kWaves == nblk - 1;
+#pragma unroll
+      for (int u = 0; u < S::PF; ++u) {
+        if (u == slot) {
+          if (tail)
+            process(std::true_type{}, kb[u], vb[u], last);
+          else
+            process(std::false_type{}, kb[u], vb[u], last);
+        }
+      }
+    }
+  }
+
+  // fused append: write the new token's row (lanes 0..NC-1: K, NC..2NC-1: V)
+  if (fuse && w == 0 && lane < 2 * S::NC) {
+    const int blk = bt_row[nblk - 1];
+    if ((unsigned)blk < (unsigned)a.num_blocks) {
+      const size_t dst = (((size_t)blk * a.hkv + kvh) * 16 + t_new) * S::RB + (lane % S::NC) * 16;
+      uint8_t* base = const_cast<uint8_t*>(lane < S::NC ? kbase : vbase);
+      *reinterpret_cast<u32x4*>(base + dst) = lane < S::NC ? k_new_c : v_new_c;
     }
   }
 
@@ -312,7 +435,7 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
       for (int e = 0; e < S::CE; e += 4)
         *reinterpret_cast<f32x4*>(dst + e) = f32x4{acc[hh][e], acc[hh][e + 1], acc[hh][e + 2], acc[hh][e + 3]};
     }
-    if (active && tq == 0) ml[w * G + h] = make_float2(m_run, l_run);
+    if (active && lane % S::LPH == 0) ml[w * G + h] = make_float2(m_run, l_run);
   }
   __syncthreads();
   for (int o = tid; o < G * D; o += kWaves * 64) {
@@ -404,20 +527,28 @@ int dispatch_decode(const DecodeArgs& a, int dtype, int D, int B, int G, hipStre
   return KVC_ERR_UNSUPPORTED;
 }
 
-// Blocks per partition: aim for >= 2048 workgroups (8 per CU) so the grid
-// fills all 256 CUs several times over, but never fewer than 16 blocks (4 per
-// wave) so each wave's prefetch pipeline has work to overlap.
+// Blocks per partition. Every partition costs a pipeline fill, an LDS merge
+// and (when a sequence has several) a partial write plus the merge pass, so a
+// sequence is split only as far as needed to give the chip about two resident
+// workgroups per CU (512 on MI355X's 256 CUs). B=64 x 8 kv heads already fills
+// that unsplit; 8 sequences at 32k tokens are split 8 ways.
+constexpr int kTargetWorkgroups = 512;
+
 int decode_part_blocks(int B, int hkv, int nblk_max) {
   static const int forced = [] {
     const char* e = getenv("KVC_DECODE_PART_BLOCKS");
     return e ? atoi(e) : 0;
   }();
-  if (forced >= kMinPartBlocks) return forced;
+  if (forced >= kMinPartBlocks) return forced < kMaxPartBlocks ? forced : kMaxPartBlocks;
   const int64_t units = (int64_t)B * hkv;
-  const int64_t want = units >= 2048 ? 1 : (2048 + units - 1) / units;
-  int64_t pb = (nblk_max + want - 1) / want;
+  int64_t n_part = (kTargetWorkgroups + units - 1) / units;
+  const int64_t max_parts = (nblk_max + kMinPartBlocks - 1) / kMinPartBlocks;
+  if (n_part > max_parts) n_part = max_parts;
+  if (n_part < 1) n_part = 1;
+  int64_t pb = (nblk_max + n_part - 1) / n_part;
   pb = (pb + 3) / 4 * 4;
   if (pb < kMinPartBlocks) pb = kMinPartBlocks;
+  if (pb > kMaxPartBlocks) pb = kMaxPartBlocks;
   return (int)pb;
 }
 
@@ -432,12 +563,13 @@ extern "C" size_t kvc_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head
   return (size_t)B * Hq * n_part_max * ((size_t)head_dim * 4 + 8);
 }
 
-extern "C" int kvc_paged_decode_attention(const kvc_cache* cache, const void* q, int32_t B, int32_t Hq,
-                                          const int32_t* block_table, int32_t max_blocks,
-                                          const int32_t* context_lens, int32_t max_context_len,
-                                          float softmax_scale, void* out, void* workspace,
-                                          size_t workspace_bytes, void* stream) {
-  int st = kvc::check_cache(cache);
+namespace kvc {
+
+static int decode_entry(const kvc_cache* cache, const void* q, const void* k_new, const void* v_new,
+                        int32_t B, int32_t Hq, const int32_t* block_table, int32_t max_blocks,
+                        const int32_t* context_lens, int32_t max_context_len, float softmax_scale,
+                        void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_cache(cache);
   if (st != KVC_OK) return st;
   if (B < 0 || Hq <= 0 || max_blocks < 0 || max_context_len < 0) return KVC_ERR_SHAPE;
   if (Hq % cache->num_kv_heads != 0) return KVC_ERR_SHAPE;
@@ -447,15 +579,17 @@ extern "C" int kvc_paged_decode_attention(const kvc_cache* cache, const void* q,
   if (B == 0) return KVC_OK;
   if (!q || !block_table || !context_lens || !out) return KVC_ERR_NULL;
 
-  const int nblk_max = (int)kvc::ceil_div(max_context_len, 16);
-  const int pb = kvc::decode_part_blocks(B, cache->num_kv_heads, nblk_max);
-  const int n_part = nblk_max > 0 ? (int)kvc::ceil_div(nblk_max, pb) : 1;
+  const int nblk_max = (int)ceil_div(max_context_len, 16);
+  const int pb = decode_part_blocks(B, cache->num_kv_heads, nblk_max);
+  const int n_part = nblk_max > 0 ? (int)ceil_div(nblk_max, pb) : 1;
   const size_t n_rows = (size_t)B * Hq * n_part;
   const size_t need = n_part > 1 ? n_rows * ((size_t)cache->head_dim * 4 + 8) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need)) return KVC_ERR_WORKSPACE;
 
-  kvc::DecodeArgs a;
+  DecodeArgs a;
   a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.kc = cache->k_cache;
   a.vc = cache->v_cache;
   a.bt = block_table;
@@ -473,5 +607,27 @@ extern "C" int kvc_paged_decode_attention(const kvc_cache* cache, const void* q,
   a.part_blocks = pb;
   a.n_part = n_part;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  return kvc::dispatch_decode(a, cache->dtype, cache->head_dim, B, G, kvc::as_stream(stream));
+  return dispatch_decode(a, cache->dtype, cache->head_dim, B, G, as_stream(stream));
+}
+
+}  // namespace kvc
+
+extern "C" int kvc_paged_decode_attention(const kvc_cache* cache, const void* q, int32_t B, int32_t Hq,
+                                          const int32_t* block_table, int32_t max_blocks,
+                                          const int32_t* context_lens, int32_t max_context_len,
+                                          float softmax_scale, void* out, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  return kvc::decode_entry(cache, q, nullptr, nullptr, B, Hq, block_table, max_blocks, context_lens,
+                           max_context_len, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int kvc_decode_append_attention(const kvc_cache* cache, const void* q, const void* k_new,
+                                           const void* v_new, int32_t B, int32_t Hq,
+                                           const int32_t* block_table, int32_t max_blocks,
+                                           const int32_t* context_lens, int32_t max_context_len,
+                                           float softmax_scale, void* out, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  if (B > 0 && (!k_new || !v_new)) return KVC_ERR_NULL;
+  return kvc::decode_entry(cache, q, k_new, v_new, B, Hq, block_table, max_blocks, context_lens,
+                           max_context_len, softmax_scale, out, workspace, workspace_bytes, stream);
 }

@@ -188,3 +188,36 @@ def test_bad_block_id_is_flagged_not_faulted(kvc):
     assert int(cache.err_flag.item()) & kvc.DEVERR_BLOCK_ID
     assert torch.isfinite(out).all()
     assert_close(out[0].cpu().numpy(), case.oracle_out([0])[0], "fp32", "row 0 unaffected")
+
+
+@pytest.mark.parametrize("dtype,g,d", [("bf16", 4, 128), ("fp32", 1, 64), ("bf16", 8, 64),
+                                       ("fp32", 2, 16)])
+def test_fused_step_equals_separate_calls(kvc, dtype, g, d):
+    """decode_append_attention == slot_mapping + kv_append + paged_decode_attention, bitwise,
+    for the cache and for the outputs; and within tolerance of the oracle."""
+    say(f"fused decode step vs separate calls {dtype} G={g} D={d}")
+    w = W.small_workload(f"fused-{dtype}-{g}-{d}", 800 + g * 10 + d, B=7, Hq=2 * g, Hkv=2, D=d,
+                         dtype=dtype, sigma=0.5)
+    ctx = np.array([1, 16, 17, 300, 2500, 33, 64])
+    case = DecodeCase(w, ctx, 320)
+    cache_a, out_a = case.run_gpu(kvc)                      # separate calls
+    # fused: same cache content before the step, then one launch
+    cache_b = kvc.PagedKVCache.allocate(320, w.Hkv, w.D, TDTYPE[dtype], fill_bits=FILL)
+    bt = torch.from_numpy(case.bt).cuda()
+    old = [b for b in range(case.B) if ctx[b] > 1]
+    seq = torch.from_numpy(np.concatenate([np.full(int(ctx[b]) - 1, b, np.int32) for b in old])).cuda()
+    pos = torch.from_numpy(np.concatenate([np.arange(int(ctx[b]) - 1, dtype=np.int32) for b in old])).cuda()
+    s = kvc.slot_mapping(bt, 320, seq, pos)
+    kvc.kv_append(cache_b, s, to_device(np.concatenate([case.k[b][:-1] for b in old]), dtype),
+                  to_device(np.concatenate([case.v[b][:-1] for b in old]), dtype))
+    kn = to_device(np.stack([case.k[b][-1] for b in range(case.B)]), dtype)
+    vn = to_device(np.stack([case.v[b][-1] for b in range(case.B)]), dtype)
+    out_b = kvc.decode_append_attention(cache_b, to_device(case.q, dtype), kn, vn, bt,
+                                        torch.from_numpy(ctx.astype(np.int32)).cuda(), int(ctx.max()))
+    torch.cuda.synchronize()
+    ib = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(cache_a.k_cache.view(ib), cache_b.k_cache.view(ib))
+    assert torch.equal(cache_a.v_cache.view(ib), cache_b.v_cache.view(ib))
+    assert torch.equal(out_a.view(ib), out_b.view(ib))
+    assert int(cache_b.err_flag.item()) == 0
+    assert_close(out_b.float().cpu().numpy(), case.oracle_out(), dtype, "fused")
