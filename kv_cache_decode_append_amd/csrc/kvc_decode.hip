@@ -21,9 +21,10 @@
 //   combines with the log-sum-exp rule.
 //
 // Per block (one contiguous (block, kv-head) tile of 16 x head_dim for K and for V):
-//   * K and V tiles arrive through 16-byte buffer loads, double-buffered in
-//     registers one block ahead. A buffer descriptor of zero bytes turns the
-//     prefetch past the wave's last block into a no-op with no memory traffic.
+//   * K and V tiles arrive through 16-byte non-temporal buffer loads (each tile
+//     is read once per step), in a register ring of 2-3 blocks per wave. A
+//     buffer descriptor of zero bytes turns the prefetch past the wave's last
+//     block into a no-op with no memory traffic.
 //   * QK: K goes to a per-wave LDS tile with an XOR swizzle of its 16-byte
 //     chunks (conflict-free row reads); lane (h, t) computes the full dot product
 //     of query head h with token t's key (bf16: v_dot2_f32_bf16, fp32: FMA), so
@@ -219,9 +220,9 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + off, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
-    for (int j = 0; j < S::NI; ++j) kb[j] = buffer_load16(rk, (uint32_t)(j * 64 + lane) * 16u);
+    for (int j = 0; j < S::NI; ++j) kb[j] = buffer_load16_stream(rk, (uint32_t)(j * 64 + lane) * 16u);
 #pragma unroll
-    for (int j = 0; j < S::NI; ++j) vb[j] = buffer_load16(rv, (uint32_t)(j * 64 + lane) * 16u);
+    for (int j = 0; j < S::NI; ++j) vb[j] = buffer_load16_stream(rv, (uint32_t)(j * 64 + lane) * 16u);
   };
 
   float m_run = -INFINITY, l_run = 0.f;

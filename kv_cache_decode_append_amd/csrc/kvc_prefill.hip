@@ -33,10 +33,12 @@
 
 namespace kvc {
 
-constexpr int kPfWaves = 4;
+constexpr int kPfWaves = 8;
+constexpr int kPfThreads = kPfWaves * 64;
 constexpr int kRowTiles = 2;                        // 16-row tiles per wave
-constexpr int kRows = kPfWaves * kRowTiles * 16;    // 128 query rows per workgroup
+constexpr int kRows = kPfWaves * kRowTiles * 16;    // 256 query rows per workgroup
 constexpr int kKeyTile = 64;                        // keys per staged tile
+constexpr int kBtCache = 2048;                      // block ids kept in LDS (32,768 keys)
 
 template <typename T> struct PfMfma;
 template <> struct PfMfma<bf16_tag> {
@@ -64,10 +66,17 @@ struct PfShape {
   static constexpr int DT = D / 16;                 // output dim tiles
   static constexpr bool BF16 = (EB == 2);
   static constexpr int VT_STRIDE = kKeyTile + 8;    // padded V^T row (elements), bf16 only
+  static constexpr int K_UNITS = kKeyTile * NC;     // 16-byte chunks of a K tile
+  static constexpr int KPT = (K_UNITS + kPfThreads - 1) / kPfThreads;
+  // V staging units: bf16 = (key pair, chunk) transposed on the way in; fp32 = chunk
+  static constexpr int V_UNITS = BF16 ? (kKeyTile / 2) * NC : K_UNITS;
+  static constexpr int VPT = (V_UNITS + kPfThreads - 1) / kPfThreads;
+  static constexpr int VCH = BF16 ? 2 : 1;          // chunks per V unit
   static constexpr int K_LDS = kKeyTile * RB;
   static constexpr int V_LDS = BF16 ? D * VT_STRIDE * 2 : kKeyTile * RB;
-  static constexpr int SMEM = K_LDS + V_LDS;
-  static_assert(kRows % G == 0, "G divides 128");
+  static constexpr int BUF = K_LDS + V_LDS;         // one staged key tile
+  static constexpr int SMEM = 2 * BUF + kBtCache * 4;
+  static_assert(kRows % G == 0, "G divides the row count");
 };
 
 struct PrefillArgs {
@@ -84,6 +93,8 @@ struct PrefillArgs {
   int32_t max_blocks;
   int32_t total;
   int32_t max_chunk;
+  int32_t n_qt;       // query tiles per sequence (grid decomposition)
+  int32_t n_work;     // n_qt * hkv * n_seqs
   float scale_log2;
 };
 
@@ -101,15 +112,22 @@ __device__ __forceinline__ void store4<bf16_tag>(void* out, size_t idx, const f3
 }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kPfWaves * 64) void prefill_attention_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillArgs a) {
   using S = PfShape<T, D, G>;
   using M = PfMfma<T>;
   using Frag = typename M::Frag;
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
-  uint8_t* k_lds = smem;
-  uint8_t* v_lds = smem + S::K_LDS;
+  int32_t* bt_lds = reinterpret_cast<int32_t*>(smem + 2 * S::BUF);
 
-  const int qt = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
+  // each XCD a contiguous run of work items; the query tiles of one (sequence,
+  // kv head) then share one L2 while they sweep the same keys.
+  const int per_xcd = gridDim.x / 8;
+  const int work = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (work >= a.n_work) return;
+  const int qt = work % a.n_qt;
+  const int kvh = (work / a.n_qt) % a.hkv;
+  const int s = work / (a.n_qt * a.hkv);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int t0 = a.cu[s];
@@ -126,6 +144,11 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_attention_kernel(Prefil
   const int n_tiles = last_pos / kKeyTile + 1;
   const int hq_all = a.hkv * G;
   const int32_t* bt_row = a.bt + (size_t)s * a.max_blocks;
+
+  // block ids of the keys this workgroup reads, cached in LDS
+  const int nb_need = (min(kv_len, n_tiles * kKeyTile) + 15) / 16;
+  for (int i = tid; i < min(nb_need, kBtCache); i += kPfThreads)
+    bt_lds[i] = i < a.max_blocks ? bt_row[i] : -1;
 
   // rows owned by this lane: r = w*32 + n*16 + l16
   int row_pos[kRowTiles];                              // absolute position (clamped)
@@ -158,6 +181,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_attention_kernel(Prefil
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt) o[n][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  __syncthreads();                                     // block-id cache ready
 
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kc);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vc);
@@ -169,7 +193,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_attention_kernel(Prefil
       flag_error(a.err, KVC_DEVERR_CONTEXT);
       return -1;
     }
-    const int blk = bt_row[lb];
+    const int blk = lb < kBtCache ? bt_lds[lb] : bt_row[lb];
     if ((unsigned)blk >= (unsigned)a.num_blocks) {
       flag_error(a.err, KVC_DEVERR_BLOCK_ID);
       return -1;
@@ -177,50 +201,79 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_attention_kernel(Prefil
     return (((int64_t)blk * a.hkv + kvh) * 16 + (key & 15)) * S::RB;
   };
 
+  // Register staging of one key tile: issued one tile ahead so the global
+  // loads overlap the MFMA work of the current tile.
+  u32x4 kr[S::KPT], vr[S::VPT][S::VCH];
+  auto load_tile = [&](int kt) {
+    const int key0 = kt * kKeyTile;
+#pragma unroll
+    for (int j = 0; j < S::KPT; ++j) {
+      const int ci = tid + j * kPfThreads;
+      kr[j] = u32x4{0u, 0u, 0u, 0u};
+      if (ci < S::K_UNITS) {
+        const int64_t off = row_off(key0 + ci / S::NC);
+        if (off >= 0) kr[j] = *reinterpret_cast<const u32x4*>(kbase + off + (ci % S::NC) * 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < S::VPT; ++j) {
+      const int u = tid + j * kPfThreads;
+#pragma unroll
+      for (int x = 0; x < S::VCH; ++x) {
+        vr[j][x] = u32x4{0u, 0u, 0u, 0u};
+        if (u < S::V_UNITS) {
+          // bf16 unit u = (key pair u % 32, chunk u / 32): a wave's transposing
+          // stores then cover all 32 key pairs and hit 64 distinct LDS banks
+          const int key = S::BF16 ? 2 * (u % (kKeyTile / 2)) + x : u / S::NC;
+          const int c = S::BF16 ? u / (kKeyTile / 2) : u % S::NC;
+          const int64_t off = row_off(key0 + key);
+          if (off >= 0) vr[j][x] = *reinterpret_cast<const u32x4*>(vbase + off + c * 16);
+        }
+      }
+    }
+  };
+  auto store_tile = [&](uint8_t* k_lds, uint8_t* v_lds) {
+#pragma unroll
+    for (int j = 0; j < S::KPT; ++j) {
+      const int ci = tid + j * kPfThreads;
+      if (ci < S::K_UNITS) {
+        const int key = ci / S::NC, c = ci % S::NC;
+        *reinterpret_cast<u32x4*>(k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)) = kr[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < S::VPT; ++j) {
+      const int u = tid + j * kPfThreads;
+      if (u >= S::V_UNITS) continue;
+      if constexpr (S::BF16) {
+        // keys (2kp, 2kp+1) x dims 8c..8c+7 -> V^T[dim][2kp .. 2kp+1], one dword per dim
+        const int kp = u % (kKeyTile / 2), c = u / (kKeyTile / 2);
+        uint32_t* vt = reinterpret_cast<uint32_t*>(v_lds);
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          const uint32_t lo = __builtin_amdgcn_perm(vr[j][1][wd], vr[j][0][wd], 0x05040100u);
+          const uint32_t hi = __builtin_amdgcn_perm(vr[j][1][wd], vr[j][0][wd], 0x07060302u);
+          vt[((c * 8 + 2 * wd) * S::VT_STRIDE + 2 * kp) / 2] = lo;
+          vt[((c * 8 + 2 * wd + 1) * S::VT_STRIDE + 2 * kp) / 2] = hi;
+        }
+      } else {
+        const int key = u / S::NC, c = u % S::NC;
+        *reinterpret_cast<u32x4*>(v_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)) = vr[j][0];
+      }
+    }
+  };
+
+  // Two LDS tile buffers: tile kt+1 is loaded during tile kt's MFMA work and
+  // stored into the other buffer right after it, so one barrier per tile both
+  // publishes tile kt+1 and frees tile kt's buffer.
+  load_tile(0);
+  store_tile(smem, smem + S::K_LDS);
+  __syncthreads();
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int key0 = kt * kKeyTile;
-    __syncthreads();                                   // previous tile fully consumed
-    // ---- stage K (row-major, chunk-swizzled) ----
-    for (int ci = tid; ci < kKeyTile * S::NC; ci += kPfWaves * 64) {
-      const int key = ci / S::NC, c = ci % S::NC;
-      const int64_t off = row_off(key0 + key);
-      u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      if (off >= 0) val = *reinterpret_cast<const u32x4*>(kbase + off + c * 16);
-      *reinterpret_cast<u32x4*>(k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)) = val;
-    }
-    // ---- stage V ----
-    if constexpr (S::BF16) {
-      // transposed: V^T[dim][key], rows padded to VT_STRIDE elements
-      uint16_t* vt = reinterpret_cast<uint16_t*>(v_lds);
-      for (int u = tid; u < (kKeyTile / 4) * S::NC; u += kPfWaves * 64) {
-        const int kq = u / S::NC, c = u % S::NC;     // keys 4kq..4kq+3, dims 8c..8c+7
-        u32x4 r4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t off = row_off(key0 + kq * 4 + j);
-          r4[j] = u32x4{0u, 0u, 0u, 0u};
-          if (off >= 0) r4[j] = *reinterpret_cast<const u32x4*>(vbase + off + c * 16);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int word = e >> 1, sh = (e & 1) * 16;
-          uint32_t x[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) x[j] = (r4[j][word] >> sh) & 0xffffu;
-          *reinterpret_cast<u32x2*>(vt + (c * 8 + e) * S::VT_STRIDE + kq * 4) =
-              u32x2{x[0] | (x[1] << 16), x[2] | (x[3] << 16)};
-        }
-      }
-    } else {
-      for (int ci = tid; ci < kKeyTile * S::NC; ci += kPfWaves * 64) {
-        const int key = ci / S::NC, c = ci % S::NC;
-        const int64_t off = row_off(key0 + key);
-        u32x4 val = u32x4{0u, 0u, 0u, 0u};
-        if (off >= 0) val = *reinterpret_cast<const u32x4*>(vbase + off + c * 16);
-        *reinterpret_cast<u32x4*>(v_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)) = val;
-      }
-    }
-    __syncthreads();
+    uint8_t* k_lds = smem + (kt & 1) * S::BUF;
+    uint8_t* v_lds = k_lds + S::K_LDS;
+    if (kt + 1 < n_tiles) load_tile(kt + 1);           // in flight during this tile's MFMA
 
     // ---- S^T = K . Q^T : 4 key tiles x kRowTiles row tiles ----
     f32x4 sacc[4][kRowTiles];
@@ -281,8 +334,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_attention_kernel(Prefil
       rs += __shfl_xor(rs, 32);
       l_run[n] = l_run[n] * alpha + rs;
       m_run[n] = m_new;
+      if (__builtin_expect(__any(alpha != 1.f), 0)) {   // wave-uniform: skip when no max moved
 #pragma unroll
-      for (int dt = 0; dt < S::DT; ++dt) o[n][dt] *= alpha;
+        for (int dt = 0; dt < S::DT; ++dt) o[n][dt] *= alpha;
+      }
     }
 
     // ---- O^T += V^T . P^T ----
@@ -325,6 +380,11 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_attention_kernel(Prefil
           }
         }
     }
+    if (kt + 1 < n_tiles) {
+      uint8_t* nk = smem + ((kt + 1) & 1) * S::BUF;
+      store_tile(nk, nk + S::K_LDS);
+    }
+    __syncthreads();
   }
 
   // ---- write rows: lane holds dims 16dt + 4g .. +3 of row l16 ----
@@ -341,11 +401,12 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_attention_kernel(Prefil
 }
 
 template <typename T, int D, int G>
-int launch_prefill(const PrefillArgs& a, int n_seqs, int max_chunk, hipStream_t st) {
+int launch_prefill(PrefillArgs a, int n_seqs, int max_chunk, hipStream_t st) {
   using S = PfShape<T, D, G>;
-  const int n_qt = (max_chunk + S::MP - 1) / S::MP;
-  hipLaunchKernelGGL((prefill_attention_kernel<T, D, G>), dim3(n_qt, a.hkv, n_seqs),
-                     dim3(kPfWaves * 64), 0, st, a);
+  a.n_qt = (max_chunk + S::MP - 1) / S::MP;
+  a.n_work = a.n_qt * a.hkv * n_seqs;
+  const int grid = (a.n_work + 7) / 8 * 8;           // whole XCD rounds
+  hipLaunchKernelGGL((prefill_attention_kernel<T, D, G>), dim3(grid), dim3(kPfThreads), 0, st, a);
   return launch_status();
 }
 
