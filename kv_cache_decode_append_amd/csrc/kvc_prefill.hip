@@ -185,20 +185,22 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
 
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kc);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vc);
-  // byte offset of token `key` (row start) of this kv head, or -1 when absent
+  // byte offset of token `key` (row start) of this kv head, or -1 when absent;
+  // contract violations are collected per lane and flagged once at the end
+  int bad = 0;
   auto row_off = [&](int key) -> int64_t {
-    if (key >= kv_len) return -1;
     const int lb = key >> 4;
-    if (lb >= a.max_blocks) {
-      flag_error(a.err, KVC_DEVERR_CONTEXT);
-      return -1;
-    }
-    const int blk = lb < kBtCache ? bt_lds[lb] : bt_row[lb];
-    if ((unsigned)blk >= (unsigned)a.num_blocks) {
-      flag_error(a.err, KVC_DEVERR_BLOCK_ID);
-      return -1;
-    }
-    return (((int64_t)blk * a.hkv + kvh) * 16 + (key & 15)) * S::RB;
+    const bool in_table = lb < a.max_blocks;
+    const int blk = !in_table ? -1 : (lb < kBtCache ? bt_lds[lb] : bt_row[lb]);
+    const bool ok_blk = (unsigned)blk < (unsigned)a.num_blocks;
+    if (key < kv_len) bad |= !in_table ? KVC_DEVERR_CONTEXT : (!ok_blk ? KVC_DEVERR_BLOCK_ID : 0);
+    return (key < kv_len && ok_blk) ? (((int64_t)blk * a.hkv + kvh) * 16 + (key & 15)) * S::RB
+                                    : (int64_t)-1;
+  };
+  // an absent row loads from the pool's first row (always valid) and is zeroed
+  auto load_row16 = [&](const uint8_t* base, int64_t off, int c) -> u32x4 {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(base + (off >= 0 ? off : 0) + c * 16);
+    return off >= 0 ? v : u32x4{0u, 0u, 0u, 0u};
   };
 
   // Register staging of one key tile: issued one tile ahead so the global
@@ -210,10 +212,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
     for (int j = 0; j < S::KPT; ++j) {
       const int ci = tid + j * kPfThreads;
       kr[j] = u32x4{0u, 0u, 0u, 0u};
-      if (ci < S::K_UNITS) {
-        const int64_t off = row_off(key0 + ci / S::NC);
-        if (off >= 0) kr[j] = *reinterpret_cast<const u32x4*>(kbase + off + (ci % S::NC) * 16);
-      }
+      if (ci < S::K_UNITS) kr[j] = load_row16(kbase, row_off(key0 + ci / S::NC), ci % S::NC);
     }
 #pragma unroll
     for (int j = 0; j < S::VPT; ++j) {
@@ -226,8 +225,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
           // stores then cover all 32 key pairs and hit 64 distinct LDS banks
           const int key = S::BF16 ? 2 * (u % (kKeyTile / 2)) + x : u / S::NC;
           const int c = S::BF16 ? u / (kKeyTile / 2) : u % S::NC;
-          const int64_t off = row_off(key0 + key);
-          if (off >= 0) vr[j][x] = *reinterpret_cast<const u32x4*>(vbase + off + c * 16);
+          vr[j][x] = load_row16(vbase, row_off(key0 + key), c);
         }
       }
     }
@@ -302,7 +300,16 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
     }
 
     // ---- online softmax per row (lane owns row l16 of each row tile) ----
-    const bool diag = key0 + kKeyTile - 1 > p0 + pos_lo;   // some key may pass some row
+    // Only tiles that reach past the smallest row position need the causal mask.
+    if (key0 + kKeyTile - 1 > p0 + pos_lo) {
+#pragma unroll
+      for (int n = 0; n < kRowTiles; ++n)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (key0 + m * 16 + g * 4 + i > row_pos[n]) sacc[m][n][i] = -INFINITY;
+    }
     float pbuf[4][kRowTiles][4];
 #pragma unroll
     for (int n = 0; n < kRowTiles; ++n) {
@@ -310,14 +317,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sacc[m][n][i];
-          if (diag && key0 + m * 16 + g * 4 + i > row_pos[n]) v = -INFINITY;
-          pbuf[m][n][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[m][n][i]);
+      mx = rows_max(mx);
       const float m_new = fmaxf(m_run[n], mx * a.scale_log2);
       const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run[n] - m_safe);
@@ -326,12 +327,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
       for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(pbuf[m][n][i], a.scale_log2, -m_safe));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[m][n][i], a.scale_log2, -m_safe));
           pbuf[m][n][i] = p;
           rs += p;
         }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
+      rs = rows_sum(rs);
       l_run[n] = l_run[n] * alpha + rs;
       m_run[n] = m_new;
       if (__builtin_expect(__any(alpha != 1.f), 0)) {   // wave-uniform: skip when no max moved
@@ -386,6 +386,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
     }
     __syncthreads();
   }
+
+  if (bad) flag_error(a.err, bad);
 
   // ---- write rows: lane holds dims 16dt + 4g .. +3 of row l16 ----
 #pragma unroll
@@ -455,6 +457,7 @@ extern "C" int kvc_chunked_prefill_attention(const kvc_cache* cache, const void*
   const int G = Hq / cache->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVC_ERR_UNSUPPORTED;
   if (n_seqs == 0 || total_tokens == 0 || max_chunk_len == 0) return KVC_OK;
+  if (cache->num_blocks < 1) return KVC_ERR_SHAPE;   // a chunk needs somewhere to go
   if (!q || !k || !v || !cu_chunk_lens || !prefix_lens || !block_table || !out) return KVC_ERR_NULL;
   hipStream_t s = kvc::as_stream(stream);
   st = kvc::launch_chunk_append(cache, k, v, n_seqs, cu_chunk_lens, prefix_lens, total_tokens,
