@@ -11,8 +11,8 @@
 // prefix caching", section "A prefix already in the cache can skip its
 // prefill"). This is the one dense contraction of the path, so it runs on MFMA.
 //
-// Tiling (one workgroup = 4 waves = 128 query rows of one kv head):
-//   row r <-> (position qt*MP + r / G, query head kvh*G + r % G), MP = 128 / G,
+// Tiling (one workgroup = 8 waves = 256 query rows of one kv head):
+//   row r <-> (position qt*MP + r / G, query head kvh*G + r % G), MP = 256 / G,
 //   so the G query heads that share a K/V head share every K/V tile.
 //   Keys are walked in tiles of 64 (four 16-token blocks through the block
 //   table). Per tile and wave (2 row tiles of 16):
@@ -24,6 +24,8 @@
 //   fp32: v_mfma_f32_16x16x4_f32 (V read row-major, one element per lane).
 //   The reduction order inside an MFMA over keys is a permutation of the keys
 //   (key 16m + 4g + i for lane group g); A and B use the same permutation.
+//   The three steps are software-pipelined across key tiles so that the
+//   softmax of one tile overlaps the PV product of the previous one.
 
 #include <math.h>
 
@@ -38,7 +40,7 @@ constexpr int kPfThreads = kPfWaves * 64;
 constexpr int kRowTiles = 2;                        // 16-row tiles per wave
 constexpr int kRows = kPfWaves * kRowTiles * 16;    // 256 query rows per workgroup
 constexpr int kKeyTile = 64;                        // keys per staged tile
-constexpr int kBtCache = 2048;                      // block ids kept in LDS (32,768 keys)
+constexpr int kWaitVmcnt0 = 0x0F70;                 // s_waitcnt vmcnt(0) (expcnt, lgkmcnt: no wait)
 
 template <typename T> struct PfMfma;
 template <> struct PfMfma<bf16_tag> {
@@ -55,6 +57,12 @@ template <> struct PfMfma<float> {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
 };
+
+// Softmax weights of one key tile as the PV product consumes them: bf16 pairs
+// packed as MFMA B fragments, or fp32 one per (key tile, row tile, element).
+template <bool BF16> struct PfP;
+template <> struct PfP<true> { struct Tile { u32x4 v[2][kRowTiles]; }; };
+template <> struct PfP<false> { struct Tile { float v[4][kRowTiles][4]; }; };
 
 template <typename T, int D, int G>
 struct PfShape {
@@ -74,8 +82,11 @@ struct PfShape {
   static constexpr int VCH = BF16 ? 2 : 1;          // chunks per V unit
   static constexpr int K_LDS = kKeyTile * RB;
   static constexpr int V_LDS = BF16 ? D * VT_STRIDE * 2 : kKeyTile * RB;
-  static constexpr int BUF = K_LDS + V_LDS;         // one staged key tile
-  static constexpr int SMEM = 2 * BUF + kBtCache * 4;
+  static constexpr int TILES = 2 * K_LDS + 2 * V_LDS;   // two K and two V tile buffers
+  // pool rows of the blocks a workgroup reads, kept in LDS: 8,192 blocks
+  // (131,072 keys) where the tile buffers leave room, else 2,048
+  static constexpr int BT_CACHE = TILES <= 96 * 1024 ? 8192 : 2048;
+  static constexpr int SMEM = TILES + BT_CACHE * 4;
   static_assert(kRows % G == 0, "G divides the row count");
 };
 
@@ -117,7 +128,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
   using M = PfMfma<T>;
   using Frag = typename M::Frag;
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
-  int32_t* bt_lds = reinterpret_cast<int32_t*>(smem + 2 * S::BUF);
+  int32_t* bt_lds = reinterpret_cast<int32_t*>(smem + S::TILES);
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
   // each XCD a contiguous run of work items; the query tiles of one (sequence,
@@ -145,10 +156,27 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
   const int hq_all = a.hkv * G;
   const int32_t* bt_row = a.bt + (size_t)s * a.max_blocks;
 
-  // block ids of the keys this workgroup reads, cached in LDS
+  // The pool row (block id * Hkv + kv head) of every block this workgroup
+  // reads, validated once and cached in LDS; -1 for a block that holds no key
+  // or has an id outside the pool. Contract violations are collected per lane
+  // and flagged once at the end.
   const int nb_need = (min(kv_len, n_tiles * kKeyTile) + 15) / 16;
-  for (int i = tid; i < min(nb_need, kBtCache); i += kPfThreads)
-    bt_lds[i] = i < a.max_blocks ? bt_row[i] : -1;
+  int bad = 0;
+  auto pool_row = [&](int lb) -> int {
+    if (lb >= nb_need) return -1;
+    if (lb >= a.max_blocks) {
+      bad |= KVC_DEVERR_CONTEXT;
+      return -1;
+    }
+    const int blk = bt_row[lb];
+    if ((unsigned)blk >= (unsigned)a.num_blocks) {
+      bad |= KVC_DEVERR_BLOCK_ID;
+      return -1;
+    }
+    return blk * a.hkv + kvh;
+  };
+  for (int i = tid; i < min(4 * (n_tiles + 1), S::BT_CACHE); i += kPfThreads)
+    bt_lds[i] = pool_row(i);
 
   // rows owned by this lane: r = w*32 + n*16 + l16
   int row_pos[kRowTiles];                              // absolute position (clamped)
@@ -185,123 +213,166 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
 
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kc);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vc);
-  // byte offset of token `key` (row start) of this kv head, or -1 when absent;
-  // contract violations are collected per lane and flagged once at the end
-  int bad = 0;
-  auto row_off = [&](int key) -> int64_t {
-    const int lb = key >> 4;
-    const bool in_table = lb < a.max_blocks;
-    const int blk = !in_table ? -1 : (lb < kBtCache ? bt_lds[lb] : bt_row[lb]);
-    const bool ok_blk = (unsigned)blk < (unsigned)a.num_blocks;
-    if (key < kv_len) bad |= !in_table ? KVC_DEVERR_CONTEXT : (!ok_blk ? KVC_DEVERR_BLOCK_ID : 0);
-    return (key < kv_len && ok_blk) ? (((int64_t)blk * a.hkv + kvh) * 16 + (key & 15)) * S::RB
-                                    : (int64_t)-1;
+  // Pool row of logical block lb of a tile that `cached` says lies inside the
+  // LDS cache (the same for the whole tile). Past the cache the row is read
+  // and checked here; that read waits for itself inside its branch, so the
+  // common path never waits for an outstanding K/V load.
+  const __amdgpu_buffer_rsrc_t bt_rsrc = make_rsrc(bt_row, (uint32_t)a.max_blocks * 4u);
+  auto block_row = [&](int lb, bool cached) -> int {
+    if (cached) return bt_lds[lb];
+    int r = -1;
+    if (lb < nb_need) {
+      if (lb >= a.max_blocks) {
+        bad |= KVC_DEVERR_CONTEXT;
+      } else {
+        const int blk = __builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, lb * 4, 0, 0);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        if ((unsigned)blk < (unsigned)a.num_blocks)
+          r = blk * a.hkv + kvh;
+        else
+          bad |= KVC_DEVERR_BLOCK_ID;
+      }
+    }
+    return r;
   };
-  // an absent row loads from the pool's first row (always valid) and is zeroed
-  auto load_row16 = [&](const uint8_t* base, int64_t off, int c) -> u32x4 {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(base + (off >= 0 ? off : 0) + c * 16);
-    return off >= 0 ? v : u32x4{0u, 0u, 0u, 0u};
+  // 16 bytes (chunk c) of key `key` of tile kt. An absent key loads from the
+  // pool's first row (always valid) and is zeroed when stored to LDS, so no
+  // wait for the load lands here.
+  struct Row16 { int64_t off; bool ok; };
+  auto locate = [&](int kt, int key, bool cached) -> Row16 {
+    const int r = block_row(kt * 4 + (key >> 4), cached);
+    const bool ok = r >= 0 && kt * kKeyTile + key < kv_len;
+    return {ok ? (int64_t)r * (16 * S::RB) + (key & 15) * S::RB : 0, ok};
   };
+  auto zero_unless = [](bool ok, const u32x4& v) { return ok ? v : u32x4{0u, 0u, 0u, 0u}; };
 
-  // Register staging of one key tile: issued one tile ahead so the global
-  // loads overlap the MFMA work of the current tile.
+  // Register staging of K and V tiles. K runs two tiles ahead of V (QK^T of
+  // tile k+1 is computed before PV of tile k), so each is loaded on its own.
+  constexpr bool kAllK = S::K_UNITS % kPfThreads == 0;   // every thread has every K unit
+  constexpr bool kAllV = S::V_UNITS % kPfThreads == 0;
   u32x4 kr[S::KPT], vr[S::VPT][S::VCH];
-  auto load_tile = [&](int kt) {
-    const int key0 = kt * kKeyTile;
+  bool kok[S::KPT], vok[S::VPT][S::VCH];
+  auto load_k = [&](int kt) {
+    const bool cached = 4 * kt < S::BT_CACHE;
 #pragma unroll
     for (int j = 0; j < S::KPT; ++j) {
       const int ci = tid + j * kPfThreads;
-      kr[j] = u32x4{0u, 0u, 0u, 0u};
-      if (ci < S::K_UNITS) kr[j] = load_row16(kbase, row_off(key0 + ci / S::NC), ci % S::NC);
+      const bool has = kAllK || ci < S::K_UNITS;
+      const Row16 rw = locate(kt, has ? ci / S::NC : 0, cached);
+      kok[j] = has && rw.ok;
+      kr[j] = *reinterpret_cast<const u32x4*>(kbase + rw.off + (ci % S::NC) * 16);
     }
+  };
+  auto load_v = [&](int kt) {
+    const bool cached = 4 * kt < S::BT_CACHE;
 #pragma unroll
     for (int j = 0; j < S::VPT; ++j) {
       const int u = tid + j * kPfThreads;
+      const bool has = kAllV || u < S::V_UNITS;
 #pragma unroll
       for (int x = 0; x < S::VCH; ++x) {
-        vr[j][x] = u32x4{0u, 0u, 0u, 0u};
-        if (u < S::V_UNITS) {
-          // bf16 unit u = (key pair u % 32, chunk u / 32): a wave's transposing
-          // stores then cover all 32 key pairs and hit 64 distinct LDS banks
-          const int key = S::BF16 ? 2 * (u % (kKeyTile / 2)) + x : u / S::NC;
-          const int c = S::BF16 ? u / (kKeyTile / 2) : u % S::NC;
-          vr[j][x] = load_row16(vbase, row_off(key0 + key), c);
-        }
+        // bf16 unit u = (key pair u % 32, chunk u / 32): a wave's transposing
+        // stores then cover all 32 key pairs and hit 64 distinct LDS banks
+        const int key = !has ? 0 : S::BF16 ? 2 * (u % (kKeyTile / 2)) + x : u / S::NC;
+        const int c = S::BF16 ? u / (kKeyTile / 2) : u % S::NC;
+        const Row16 rw = locate(kt, key, cached);
+        vok[j][x] = has && rw.ok;
+        vr[j][x] = *reinterpret_cast<const u32x4*>(vbase + rw.off + c * 16);
       }
     }
   };
-  auto store_tile = [&](uint8_t* k_lds, uint8_t* v_lds) {
+  auto store_k = [&](uint8_t* k_lds) {
 #pragma unroll
     for (int j = 0; j < S::KPT; ++j) {
       const int ci = tid + j * kPfThreads;
-      if (ci < S::K_UNITS) {
+      if (kAllK || ci < S::K_UNITS) {
         const int key = ci / S::NC, c = ci % S::NC;
-        *reinterpret_cast<u32x4*>(k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)) = kr[j];
+        *reinterpret_cast<u32x4*>(k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)) =
+            zero_unless(kok[j], kr[j]);
       }
     }
+  };
+  auto store_v = [&](uint8_t* v_lds) {
 #pragma unroll
     for (int j = 0; j < S::VPT; ++j) {
       const int u = tid + j * kPfThreads;
-      if (u >= S::V_UNITS) continue;
+      if (!kAllV && u >= S::V_UNITS) continue;
+      const u32x4 v0 = zero_unless(vok[j][0], vr[j][0]);
+      const u32x4 v1 = zero_unless(vok[j][S::VCH - 1], vr[j][S::VCH - 1]);
       if constexpr (S::BF16) {
         // keys (2kp, 2kp+1) x dims 8c..8c+7 -> V^T[dim][2kp .. 2kp+1], one dword per dim
         const int kp = u % (kKeyTile / 2), c = u / (kKeyTile / 2);
         uint32_t* vt = reinterpret_cast<uint32_t*>(v_lds);
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd) {
-          const uint32_t lo = __builtin_amdgcn_perm(vr[j][1][wd], vr[j][0][wd], 0x05040100u);
-          const uint32_t hi = __builtin_amdgcn_perm(vr[j][1][wd], vr[j][0][wd], 0x07060302u);
+          const uint32_t lo = __builtin_amdgcn_perm(v1[wd], v0[wd], 0x05040100u);
+          const uint32_t hi = __builtin_amdgcn_perm(v1[wd], v0[wd], 0x07060302u);
           vt[((c * 8 + 2 * wd) * S::VT_STRIDE + 2 * kp) / 2] = lo;
           vt[((c * 8 + 2 * wd + 1) * S::VT_STRIDE + 2 * kp) / 2] = hi;
         }
       } else {
         const int key = u / S::NC, c = u % S::NC;
-        *reinterpret_cast<u32x4*>(v_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)) = vr[j][0];
+        *reinterpret_cast<u32x4*>(v_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)) = v0;
       }
     }
   };
 
-  // Two LDS tile buffers: tile kt+1 is loaded during tile kt's MFMA work and
-  // stored into the other buffer right after it, so one barrier per tile both
-  // publishes tile kt+1 and frees tile kt's buffer.
-  load_tile(0);
-  store_tile(smem, smem + S::K_LDS);
-  __syncthreads();
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int key0 = kt * kKeyTile;
-    uint8_t* k_lds = smem + (kt & 1) * S::BUF;
-    uint8_t* v_lds = k_lds + S::K_LDS;
-    if (kt + 1 < n_tiles) load_tile(kt + 1);           // in flight during this tile's MFMA
-
-    // ---- S^T = K . Q^T : 4 key tiles x kRowTiles row tiles ----
-    f32x4 sacc[4][kRowTiles];
+  // ---- S^T = K . Q^T for one key tile: 4 key tiles x kRowTiles row tiles.
+  // The K fragments of key tile m+1 are read from LDS while tile m multiplies.
+  auto load_kf = [&](const uint8_t* k_lds, int m, Frag (&kf)[S::KS]) {
+    const int key = m * 16 + l16;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int n = 0; n < kRowTiles; ++n) sacc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int key = m * 16 + l16;
-#pragma unroll
-      for (int kk = 0; kk < S::KS; ++kk) {
-        Frag kf;
-        if constexpr (S::BF16) {
-          const int c = kk * 4 + g;
-          kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
-                                                k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)));
-        } else {
-          const int c = kk;                          // dims 4kk .. 4kk+3, element g
-          kf = *reinterpret_cast<const float*>(k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4) +
-                                               g * 4);
-        }
-#pragma unroll
-        for (int n = 0; n < kRowTiles; ++n) sacc[m][n] = M::mma(kf, qf[n][kk], sacc[m][n]);
+    for (int kk = 0; kk < S::KS; ++kk) {
+      if constexpr (S::BF16) {
+        const int c = kk * 4 + g;
+        kf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
+                                                  k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)));
+      } else {
+        const int c = kk;                            // dims 4kk .. 4kk+3, element g
+        kf[kk] = *reinterpret_cast<const float*>(k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4) +
+                                                 g * 4);
       }
     }
-
-    // ---- online softmax per row (lane owns row l16 of each row tile) ----
-    // Only tiles that reach past the smallest row position need the causal mask.
-    if (key0 + kKeyTile - 1 > p0 + pos_lo) {
+  };
+  auto qk = [&](const uint8_t* k_lds, f32x4 (&sacc)[4][kRowTiles]) {
+    if constexpr (S::BF16) {
+      // steps (m, kk); the fragment of step st+kAhead is read while step st
+      // multiplies, and a scheduling fence per step keeps that order
+      constexpr int kSteps = 4 * S::KS, kAhead = 3;
+      bf16x8_t kf[kAhead + 1];
+      auto frag = [&](int st) {
+        const int key = (st / S::KS) * 16 + l16, c = (st % S::KS) * 4 + g;
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
+                                                k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)));
+      };
+#pragma unroll
+      for (int st = 0; st < kAhead; ++st) kf[st] = frag(st);
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        if (st + kAhead < kSteps) kf[(st + kAhead) % (kAhead + 1)] = frag(st + kAhead);
+        const int m = st / S::KS, kk = st % S::KS;
+#pragma unroll
+        for (int n = 0; n < kRowTiles; ++n)
+          sacc[m][n] = M::mma(kf[st % (kAhead + 1)], qf[n][kk],
+                              kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[m][n]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        Frag kf[S::KS];
+        load_kf(k_lds, m, kf);
+#pragma unroll
+        for (int kk = 0; kk < S::KS; ++kk)
+#pragma unroll
+          for (int n = 0; n < kRowTiles; ++n)
+            sacc[m][n] = M::mma(kf[kk], qf[n][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[m][n]);
+      }
+    }
+  };
+  // causal mask, only for tiles that reach past the smallest row position
+  auto mask = [&](f32x4 (&sacc)[4][kRowTiles], int key0) {
+    if (__builtin_expect(key0 + kKeyTile - 1 > p0 + pos_lo, 0)) {
 #pragma unroll
       for (int n = 0; n < kRowTiles; ++n)
 #pragma unroll
@@ -310,7 +381,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
           for (int i = 0; i < 4; ++i)
             if (key0 + m * 16 + g * 4 + i > row_pos[n]) sacc[m][n][i] = -INFINITY;
     }
-    float pbuf[4][kRowTiles][4];
+  };
+  // ---- online softmax of one tile (lane owns row l16 of each row tile).
+  // Row sums stay per lane (a partial over this lane's keys) until the end;
+  // the running max is reduced across the row every tile.
+  using PTile = typename PfP<S::BF16>::Tile;
+  auto softmax = [&](const f32x4 (&sacc)[4][kRowTiles], PTile& pt, float (&alpha)[kRowTiles]) {
 #pragma unroll
     for (int n = 0; n < kRowTiles; ++n) {
       float mx = -INFINITY;
@@ -321,48 +397,52 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
       mx = rows_max(mx);
       const float m_new = fmaxf(m_run[n], mx * a.scale_log2);
       const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[n] - m_safe);
+      alpha[n] = __builtin_amdgcn_exp2f(m_run[n] - m_safe);
+      m_run[n] = m_new;
+      float p[4][4];
       float rs = 0.f;
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[m][n][i], a.scale_log2, -m_safe));
-          pbuf[m][n][i] = p;
-          rs += p;
+          p[m][i] = __builtin_amdgcn_exp2f(fmaf(sacc[m][n][i], a.scale_log2, -m_safe));
+          rs += p[m][i];
         }
-      rs = rows_sum(rs);
-      l_run[n] = l_run[n] * alpha + rs;
-      m_run[n] = m_new;
-      if (__builtin_expect(__any(alpha != 1.f), 0)) {   // wave-uniform: skip when no max moved
+      l_run[n] = fmaf(l_run[n], alpha[n], rs);
+      if constexpr (S::BF16) {
 #pragma unroll
-        for (int dt = 0; dt < S::DT; ++dt) o[n][dt] *= alpha;
+        for (int mp = 0; mp < 2; ++mp)
+          pt.v[mp][n] = u32x4{pack_bf16x2(p[2 * mp][0], p[2 * mp][1]),
+                              pack_bf16x2(p[2 * mp][2], p[2 * mp][3]),
+                              pack_bf16x2(p[2 * mp + 1][0], p[2 * mp + 1][1]),
+                              pack_bf16x2(p[2 * mp + 1][2], p[2 * mp + 1][3])};
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pt.v[m][n][i] = p[m][i];
       }
     }
-
-    // ---- O^T += V^T . P^T ----
+  };
+  // ---- O^T += V^T . P^T for one tile; V fragments are read one step ahead
+  auto pv = [&](const uint8_t* v_lds, const PTile& pt) {
     if constexpr (S::BF16) {
       const uint16_t* vt = reinterpret_cast<const uint16_t*>(v_lds);
+      auto load_vf = [&](int mp, int dt) -> Frag {
+        const uint16_t* rowp = vt + (dt * 16 + l16) * S::VT_STRIDE + mp * 32 + g * 4;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(rowp);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(rowp + 16);
+        return __builtin_bit_cast(bf16x8_t, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      };
+      Frag vf[2];
+      vf[0] = load_vf(0, 0);
 #pragma unroll
-      for (int mp = 0; mp < 2; ++mp) {                 // key tiles (2mp, 2mp+1) = 32 keys
-        Frag pf[kRowTiles];
+      for (int st = 0; st < 2 * S::DT; ++st) {          // st = (mp, dt)
+        const int mp = st / S::DT, dt = st % S::DT;
+        if (st + 1 < 2 * S::DT) vf[(st + 1) & 1] = load_vf((st + 1) / S::DT, (st + 1) % S::DT);
 #pragma unroll
-        for (int n = 0; n < kRowTiles; ++n) {
-          const float* a0 = pbuf[2 * mp][n];
-          const float* a1 = pbuf[2 * mp + 1][n];
-          const u32x4 pk = u32x4{pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]),
-                                 pack_bf16x2(a1[0], a1[1]), pack_bf16x2(a1[2], a1[3])};
-          pf[n] = __builtin_bit_cast(bf16x8_t, pk);
-        }
-#pragma unroll
-        for (int dt = 0; dt < S::DT; ++dt) {
-          const uint16_t* rowp = vt + (dt * 16 + l16) * S::VT_STRIDE + mp * 32 + g * 4;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(rowp);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(rowp + 16);
-          const Frag vf = __builtin_bit_cast(bf16x8_t, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-          for (int n = 0; n < kRowTiles; ++n) o[n][dt] = M::mma(vf, pf[n], o[n][dt]);
-        }
+        for (int n = 0; n < kRowTiles; ++n)
+          o[n][dt] = M::mma(vf[st & 1], __builtin_bit_cast(bf16x8_t, pt.v[mp][n]), o[n][dt]);
       }
     } else {
 #pragma unroll
@@ -376,27 +456,154 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
             const float vf = *reinterpret_cast<const float*>(
                 v_lds + key * S::RB + ((c ^ (key % S::NC)) << 4) + (dim & 3) * 4);
 #pragma unroll
-            for (int n = 0; n < kRowTiles; ++n) o[n][dt] = M::mma(vf, pbuf[m][n][i], o[n][dt]);
+            for (int n = 0; n < kRowTiles; ++n) o[n][dt] = M::mma(vf, pt.v[m][n][i], o[n][dt]);
           }
         }
     }
-    if (kt + 1 < n_tiles) {
-      uint8_t* nk = smem + ((kt + 1) & 1) * S::BUF;
-      store_tile(nk, nk + S::K_LDS);
+  };
+  // bf16: PV of one tile fused with the softmax of the next, one PV step
+  // (a V fragment times both row tiles) at a time with a slice of the softmax
+  // after it, each step fenced so the vector work stays between the MFMAs.
+  // Softmax units: 0, 1 = partial row max of row tile 0, 1; 2 = max across
+  // the row, new running max and rescale factor; 3 + e = weight e (row tile
+  // e / 16, key tile (e / 4) % 4, element e % 4), packed to bf16 in pairs.
+  auto pv_softmax = [&](const uint8_t* v_lds, const PTile& pt, const f32x4 (&sc)[4][kRowTiles],
+                        PTile& pn, float (&alpha)[kRowTiles]) {
+    if constexpr (S::BF16) {
+      constexpr int kSteps = 2 * S::DT, kAhead = 2;
+      constexpr int kUnits = 3 + 16 * kRowTiles;
+      const uint16_t* vt = reinterpret_cast<const uint16_t*>(v_lds);
+      auto frag = [&](int st) {
+        const int mp = st / S::DT, dt = st % S::DT;
+        const uint16_t* rowp = vt + (dt * 16 + l16) * S::VT_STRIDE + mp * 32 + g * 4;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(rowp);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(rowp + 16);
+        return __builtin_bit_cast(bf16x8_t, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      };
+      float mx[kRowTiles], msafe[kRowTiles], rs[kRowTiles], pw[kRowTiles][4][4];
+      auto unit = [&](int u) {
+        if (u < kRowTiles) {
+          float v = -INFINITY;
+  #pragma unroll
+          for (int m = 0; m < 4; ++m)
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) v = fmaxf(v, sc[m][u][i]);
+          mx[u] = v;
+        } else if (u == kRowTiles) {
+  #pragma unroll
+          for (int n = 0; n < kRowTiles; ++n) {
+            const float m_new = fmaxf(m_run[n], rows_max(mx[n]) * a.scale_log2);
+            msafe[n] = (m_new == -INFINITY) ? 0.f : m_new;
+            alpha[n] = __builtin_amdgcn_exp2f(m_run[n] - msafe[n]);
+            m_run[n] = m_new;
+            rs[n] = 0.f;
+          }
+        } else {
+          const int e = u - kRowTiles - 1, n = e / 16, m = (e / 4) % 4, i = e % 4;
+          pw[n][m][i] = __builtin_amdgcn_exp2f(fmaf(sc[m][n][i], a.scale_log2, -msafe[n]));
+          rs[n] += pw[n][m][i];
+          if (i & 1) pn.v[m / 2][n][(m % 2) * 2 + i / 2] = pack_bf16x2(pw[n][m][i - 1], pw[n][m][i]);
+        }
+      };
+      bf16x8_t vf[kAhead + 1];
+  #pragma unroll
+      for (int st = 0; st < kAhead; ++st) vf[st] = frag(st);
+  #pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        if (st + kAhead < kSteps) vf[(st + kAhead) % (kAhead + 1)] = frag(st + kAhead);
+        const int mp = st / S::DT, dt = st % S::DT;
+  #pragma unroll
+        for (int n = 0; n < kRowTiles; ++n)
+          o[n][dt] = M::mma(vf[st % (kAhead + 1)], __builtin_bit_cast(bf16x8_t, pt.v[mp][n]), o[n][dt]);
+  #pragma unroll
+        for (int u = 0; u < kUnits; ++u)
+          if (u * kSteps / kUnits == st) unit(u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  #pragma unroll
+      for (int n = 0; n < kRowTiles; ++n) l_run[n] = fmaf(l_run[n], alpha[n], rs[n]);
     }
-    __syncthreads();
+  };
+  auto rescale = [&](const float (&alpha)[kRowTiles]) {
+#pragma unroll
+    for (int n = 0; n < kRowTiles; ++n)
+      if (__builtin_expect(__any(alpha[n] != 1.f), 0)) {   // wave-uniform: skip when no max moved
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt) o[n][dt] *= alpha[n];
+      }
+  };
+
+  // Barrier for LDS hand-off only: waits for this wave's LDS operations, not
+  // for its outstanding global loads (which a full fence would drain).
+  auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // Software pipeline over key tiles. Iteration kt holds K(kt+1) and V(kt) in
+  // LDS and P(kt) in registers: it multiplies QK^T of tile kt+1 on MFMA, then
+  // PV of tile kt on MFMA while the softmax of tile kt+1 runs on the vector
+  // ALUs, and applies tile kt+1's rescale after PV(kt). K(kt+2) and V(kt+1)
+  // are loaded during the iteration and stored behind it; K and V each have
+  // two LDS buffers, and the barrier closing an iteration publishes the new
+  // tiles after every wave has finished with the ones they overwrite.
+  auto kbuf = [&](int i) { return smem + (i & 1) * S::K_LDS; };
+  auto vbuf = [&](int i) { return smem + 2 * S::K_LDS + (i & 1) * S::V_LDS; };
+  f32x4 sacc[4][kRowTiles];
+  PTile pt;
+  float alpha[kRowTiles];
+  load_k(0);
+  load_v(0);
+  store_k(kbuf(0));
+  store_v(vbuf(0));
+  if (n_tiles > 1) {
+    load_k(1);
+    store_k(kbuf(1));
   }
+  lds_barrier();
+  qk(kbuf(0), sacc);
+  mask(sacc, 0);
+  softmax(sacc, pt, alpha);                           // o is still zero: no rescale
+  lds_barrier();                                       // K(0) read by every wave
+  for (int kt = 0; kt + 1 < n_tiles; ++kt) {
+    const bool more_k = kt + 2 < n_tiles;
+    if (more_k) load_k(kt + 2);
+    load_v(kt + 1);
+    qk(kbuf(kt + 1), sacc);
+    mask(sacc, (kt + 1) * kKeyTile);
+    PTile pt_next;
+    if constexpr (S::BF16) {
+      pv_softmax(vbuf(kt), pt, sacc, pt_next, alpha);
+      // the next tile's weights and row sums are computed between the PV
+      // MFMAs; pin them there so they are not sunk past the rescale branch
+#pragma unroll
+      for (int mp = 0; mp < 2; ++mp)
+#pragma unroll
+        for (int n = 0; n < kRowTiles; ++n) asm volatile("" : "+v"(pt_next.v[mp][n]));
+#pragma unroll
+      for (int n = 0; n < kRowTiles; ++n) asm volatile("" : "+v"(l_run[n]));
+    } else {
+      pv(vbuf(kt), pt);
+      softmax(sacc, pt_next, alpha);
+    }
+    rescale(alpha);
+    pt = pt_next;
+    if (more_k) store_k(kbuf(kt));
+    store_v(vbuf(kt + 1));
+    lds_barrier();
+  }
+  pv(vbuf(n_tiles - 1), pt);
 
   if (bad) flag_error(a.err, bad);
 
   // ---- write rows: lane holds dims 16dt + 4g .. +3 of row l16 ----
+  float l_row[kRowTiles];
+#pragma unroll
+  for (int n = 0; n < kRowTiles; ++n) l_row[n] = rows_sum(l_run[n]);   // whole wave, before any exit
 #pragma unroll
   for (int n = 0; n < kRowTiles; ++n) {
     if (!row_ok[n]) continue;
     const int r = w * (kRowTiles * 16) + n * 16 + l16;
     const int pl = pos_lo + r / G, h = r % G;
     const size_t orow = ((size_t)(t0 + pl) * hq_all + kvh * G + h) * D;
-    const float inv = 1.f / l_run[n];
+    const float inv = 1.f / l_row[n];
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt) store4<T>(a.out, orow + dt * 16 + g * 4, o[n][dt], inv);
   }
