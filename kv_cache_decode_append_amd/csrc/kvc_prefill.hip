@@ -41,6 +41,7 @@ constexpr int kRowTiles = 2;                        // 16-row tiles per wave
 constexpr int kRows = kPfWaves * kRowTiles * 16;    // 256 query rows per workgroup
 constexpr int kKeyTile = 64;                        // keys per staged tile
 constexpr int kWaitVmcnt0 = 0x0F70;                 // s_waitcnt vmcnt(0) (expcnt, lgkmcnt: no wait)
+constexpr uint32_t kBf16OnePair = 0x3F803F80u;      // bf16 (1, 1)
 
 template <typename T> struct PfMfma;
 template <> struct PfMfma<bf16_tag> {
@@ -252,15 +253,23 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
   constexpr bool kAllV = S::V_UNITS % kPfThreads == 0;
   u32x4 kr[S::KPT], vr[S::VPT][S::VCH];
   bool kok[S::KPT], vok[S::VPT][S::VCH];
+  // A wave's K units cover 64 / NC <= 16 consecutive keys starting at a
+  // multiple of 64 / NC, so they sit in one block: its base is a scalar, and
+  // the lane's offset inside the block does not change between tiles. A unit
+  // of an absent block reads inside the pool's first block (always valid).
+  static_assert(16 % (64 / S::NC) == 0, "a wave's K rows stay in one block");
   auto load_k = [&](int kt) {
     const bool cached = 4 * kt < S::BT_CACHE;
 #pragma unroll
     for (int j = 0; j < S::KPT; ++j) {
       const int ci = tid + j * kPfThreads;
       const bool has = kAllK || ci < S::K_UNITS;
-      const Row16 rw = locate(kt, has ? ci / S::NC : 0, cached);
-      kok[j] = has && rw.ok;
-      kr[j] = *reinterpret_cast<const u32x4*>(kbase + rw.off + (ci % S::NC) * 16);
+      const int key = has ? ci / S::NC : 0;
+      const int r = __builtin_amdgcn_readfirstlane(
+          block_row(kt * 4 + __builtin_amdgcn_readfirstlane(key >> 4), cached));
+      const uint8_t* base = kbase + (r >= 0 ? (int64_t)r * (16 * S::RB) : 0);
+      kok[j] = has && r >= 0 && kt * kKeyTile + key < kv_len;
+      kr[j] = *reinterpret_cast<const u32x4*>(base + (key & 15) * S::RB + (ci % S::NC) * 16);
     }
   };
   auto load_v = [&](int kt) {
@@ -406,22 +415,26 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           p[m][i] = __builtin_amdgcn_exp2f(fmaf(sacc[m][n][i], a.scale_log2, -m_safe));
-          rs += p[m][i];
+          if constexpr (!S::BF16) rs += p[m][i];
         }
-      l_run[n] = fmaf(l_run[n], alpha[n], rs);
       if constexpr (S::BF16) {
+        // the row sum adds the bf16 weights the PV product uses
 #pragma unroll
-        for (int mp = 0; mp < 2; ++mp)
+        for (int mp = 0; mp < 2; ++mp) {
           pt.v[mp][n] = u32x4{pack_bf16x2(p[2 * mp][0], p[2 * mp][1]),
                               pack_bf16x2(p[2 * mp][2], p[2 * mp][3]),
                               pack_bf16x2(p[2 * mp + 1][0], p[2 * mp + 1][1]),
                               pack_bf16x2(p[2 * mp + 1][2], p[2 * mp + 1][3])};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) rs = dot2_bf16(pt.v[mp][n][q], kBf16OnePair, rs);
+        }
       } else {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
           for (int i = 0; i < 4; ++i) pt.v[m][n][i] = p[m][i];
       }
+      l_run[n] = fmaf(l_run[n], alpha[n], rs);
     }
   };
   // ---- O^T += V^T . P^T for one tile; V fragments are read one step ahead
@@ -501,8 +514,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
         } else {
           const int e = u - kRowTiles - 1, n = e / 16, m = (e / 4) % 4, i = e % 4;
           pw[n][m][i] = __builtin_amdgcn_exp2f(fmaf(sc[m][n][i], a.scale_log2, -msafe[n]));
-          rs[n] += pw[n][m][i];
-          if (i & 1) pn.v[m / 2][n][(m % 2) * 2 + i / 2] = pack_bf16x2(pw[n][m][i - 1], pw[n][m][i]);
+          if (i & 1) {
+            const uint32_t pair = pack_bf16x2(pw[n][m][i - 1], pw[n][m][i]);
+            pn.v[m / 2][n][(m % 2) * 2 + i / 2] = pair;
+            rs[n] = dot2_bf16(pair, kBf16OnePair, rs[n]);   // sum of the weights PV uses
+          }
         }
       };
       bf16x8_t vf[kAhead + 1];
