@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--workload", default="c3-decode",
-                    choices=["c3-decode", "c5-decode", "c5-prefill"])
+                    choices=["c3-decode", "c5-decode", "c5-prefill", "prefix-warm"])
     return ap.parse_args()
 
 
@@ -144,6 +144,8 @@ def main():
         return bench_c5_decode(args)
     if args.workload == "c5-prefill":
         return bench_c5_prefill(args)
+    if args.workload == "prefix-warm":
+        return bench_prefix_warm(args)
 
     import torch
 
@@ -369,6 +371,82 @@ def bench_c5_prefill(args):
                       "frac": round(tf / 2500.0, 4), "traffic": None,
                       "avg_us": round(ms * 1e3, 1), "flop_per_launch": flop})
     res["steps"] = steps
+    print(json.dumps(res), flush=True)
+
+
+def bench_prefix_warm(args):
+    """Prefix caching at the Llama-3.1-8B attention shape: a 2,000-token prompt
+    whose first 1,800 tokens are already cached. Cold = chunked prefill of all
+    2,000 tokens; warm = block match in the native manager, then prefill of the
+    208 tokens after the 112 cached blocks (1,792 tokens). Each is one launch
+    per layer over 32 layer pools; the match is timed on the host."""
+    import torch
+
+    import kv_cache_decode_append_amd as kvc
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = W.P1
+    n, Hq, Hkv, D, L = W.P1_PROMPT, w.Hq, w.Hkv, w.D, w.layers
+    A, B = W.shared_prompts(2)
+    nblk = W.blocks_for(n)
+    pc = kvc.PrefixCache(2 * nblk)
+    ba = pc.allocate(nblk)
+    pc.commit(A, ba)
+    t0 = time.perf_counter()
+    reps = 200
+    for _ in range(reps):
+        m = pc.match(B)
+        pc.release(m)
+    match_us = (time.perf_counter() - t0) / reps * 1e6
+    m = pc.match(B)
+    start = 16 * len(m)
+    fresh = pc.allocate(nblk - len(m))
+    caches = [kvc.PagedKVCache.allocate(2 * nblk, Hkv, D, torch.bfloat16, device=dev)
+              for _ in range(L)]
+    for c in caches:
+        c.k_cache.normal_(0, 0.5)
+        c.v_cache.normal_(0, 0.5)
+    q = torch.empty(n, Hq, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
+    k = torch.empty(n, Hkv, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
+    v = torch.empty_like(k)
+    out = torch.empty_like(q)
+    bt_cold = torch.tensor([ba], dtype=torch.int32, device=dev)
+    bt_warm = torch.tensor([m + fresh], dtype=torch.int32, device=dev)
+    cu_cold = torch.tensor([0, n], dtype=torch.int32, device=dev)
+    cu_warm = torch.tensor([0, n - start], dtype=torch.int32, device=dev)
+    p_cold = torch.zeros(1, dtype=torch.int32, device=dev)
+    p_warm = torch.full((1,), start, dtype=torch.int32, device=dev)
+
+    def cold(i):
+        for c in caches:
+            kvc.chunked_prefill_attention(c, q, k, v, cu_cold, p_cold, bt_cold, n, out=out)
+
+    def warm(i):
+        for c in caches:
+            kvc.chunked_prefill_attention(c, q[start:], k[start:], v[start:], cu_warm, p_warm,
+                                          bt_warm, n - start, out=out[start:])
+
+    ms_cold = _timed(cold, args.steps, args.warmup)
+    ms_warm = _timed(warm, args.steps, args.warmup)
+    pairs_cold = Hq * n * (n + 1) // 2
+    pairs_warm = Hq * ((n - start) * start + (n - start) * (n - start + 1) // 2)
+    res = _base_line(args, "prefix-cached prefill attention time, 2,000-token prompt with 1,800 "
+                     "tokens cached, 32 layers (warm)", round(ms_warm, 4), "ms", ms_warm, "bf16",
+                     {"workload": "one 2,000-token prompt, first 1,800 tokens shared with a cached "
+                                  "prompt, GQA 32/8, head_dim 128, bf16, 32 layers",
+                      "prompt": n, "shared": W.P1_SHARED, "matched_blocks": len(m),
+                      "prefill_start": start, "layers": L},
+                     {"bound": "mfma", "kernel": "chunk_append_kernel + prefill_attention_kernel",
+                      "achieved": round(pairs_warm * 4 * D * L / (ms_warm * 1e-3) / 1e12, 1),
+                      "peak": 2500.0, "unit": "TFLOP/s",
+                      "frac": round(pairs_warm * 4 * D * L / (ms_warm * 1e-3) / 2.5e15, 4),
+                      "traffic": None, "avg_us": round(ms_warm * 1e3 / L, 2)})
+    res["higher_is_better"] = False
+    res["cold_ms"] = round(ms_cold, 4)
+    res["cold_tflops"] = round(pairs_cold * 4 * D * L / (ms_cold * 1e-3) / 1e12, 1)
+    res["speedup_cold_over_warm"] = round(ms_cold / ms_warm, 2)
+    res["host_match_us"] = round(match_us, 1)
     print(json.dumps(res), flush=True)
 
 

@@ -1,6 +1,7 @@
 """Paged KV-cache append, GQA decode attention and chunked-prefill attention on
 AMD MI355X (gfx950): HIP kernels behind the C ABI in include/kvc.h, with this
-thin binding on top. Importing the package loads libkvc.so and raises if it is
+thin binding on top, and a host-side prefix-caching block manager
+(include/kvc_prefix.h). Importing the package loads libkvc.so and raises if it is
 missing; there is no CPU fallback.
 """
 from ._lib import (  # noqa: F401
@@ -14,6 +15,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     KvcError,
     PagedKVCache,
+    PrefixCache,
     chunked_prefill_attention,
     decode_append_attention,
     decode_workspace_bytes,

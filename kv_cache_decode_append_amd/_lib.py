@@ -80,6 +80,14 @@ def _load() -> ctypes.CDLL:
         "kvc_chunked_prefill_attention": (c_int, [P, vp, vp, vp, c_i32, vp, vp, c_i32, c_i32, vp,
                                                   c_i32, c_i32, fl, vp, vp]),
         "kvc_status_string": (ctypes.c_char_p, [c_int]),
+        "kvc_prefix_cache_create": (vp, [c_i32, c_i32]),
+        "kvc_prefix_cache_destroy": (None, [vp]),
+        "kvc_prefix_cache_match": (c_i32, [vp, vp, c_i32, vp, c_i32]),
+        "kvc_prefix_cache_allocate": (c_i32, [vp, c_i32, vp]),
+        "kvc_prefix_cache_commit": (c_i32, [vp, vp, c_i32, vp, c_i32]),
+        "kvc_prefix_cache_release": (c_i32, [vp, vp, c_i32]),
+        "kvc_prefix_cache_refcount": (c_i32, [vp, c_i32]),
+        "kvc_prefix_cache_counts": (c_i32, [vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -287,3 +295,68 @@ def chunked_prefill_attention(cache: PagedKVCache, q: torch.Tensor, k: torch.Ten
         prefix_lens.data_ptr(), total, int(max_chunk_len), block_table.data_ptr(),
         block_table.shape[1], Hq, scale, out.data_ptr(), _stream()))
     return out
+
+
+KVC_ERR_NO_BLOCKS = -7
+
+
+class PrefixCache:
+    """Host-side block manager with prefix matching (include/kvc_prefix.h).
+
+    Block ids index the first dimension of every layer's pool. ``match`` and
+    ``allocate`` take references, ``release`` drops them, ``commit`` makes a
+    sequence's full blocks matchable once their K/V are written."""
+
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE):
+        self._h = LIB.kvc_prefix_cache_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise KvcError("kvc_prefix_cache_create", -2, "bad pool shape or out of memory")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            LIB.kvc_prefix_cache_destroy(h)
+
+    @staticmethod
+    def _ints(xs):
+        a = (ctypes.c_int32 * max(1, len(xs)))(*[int(x) for x in xs])
+        return a
+
+    def match(self, tokens, max_blocks: int | None = None) -> list[int]:
+        toks = self._ints(tokens)
+        cap = (len(tokens) // self.block_size) if max_blocks is None else int(max_blocks)
+        out = (ctypes.c_int32 * max(1, cap))()
+        n = LIB.kvc_prefix_cache_match(self._h, toks, len(tokens), out, cap)
+        _check("kvc_prefix_cache_match", min(n, 0))
+        return list(out[:n])
+
+    def allocate(self, n: int) -> list[int] | None:
+        """``n`` new blocks, or None when the pool cannot supply them."""
+        out = (ctypes.c_int32 * max(1, n))()
+        got = LIB.kvc_prefix_cache_allocate(self._h, int(n), out)
+        if got == KVC_ERR_NO_BLOCKS:
+            return None
+        _check("kvc_prefix_cache_allocate", min(got, 0))
+        return list(out[:n])
+
+    def commit(self, tokens, block_ids) -> None:
+        _check("kvc_prefix_cache_commit", LIB.kvc_prefix_cache_commit(
+            self._h, self._ints(tokens), len(tokens), self._ints(block_ids), len(block_ids)))
+
+    def release(self, block_ids) -> None:
+        _check("kvc_prefix_cache_release", LIB.kvc_prefix_cache_release(
+            self._h, self._ints(block_ids), len(block_ids)))
+
+    def refcount(self, block_id: int) -> int:
+        r = LIB.kvc_prefix_cache_refcount(self._h, int(block_id))
+        _check("kvc_prefix_cache_refcount", min(r, 0))
+        return r
+
+    def counts(self) -> tuple[int, int, int]:
+        """(free, cached, referenced) block counts."""
+        f, c, r = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check("kvc_prefix_cache_counts", LIB.kvc_prefix_cache_counts(
+            self._h, ctypes.byref(f), ctypes.byref(c), ctypes.byref(r)))
+        return f.value, c.value, r.value

@@ -20,6 +20,8 @@ extern "C" const char* kvc_status_string(int status) {
     case KVC_ERR_UNSUPPORTED: return "unsupported head_dim, block_size or head grouping";
     case KVC_ERR_WORKSPACE: return "workspace missing or too small";
     case KVC_ERR_LAUNCH: return "kernel launch failed";
+    case KVC_ERR_NO_BLOCKS: return "not enough free or reusable blocks";
+    case KVC_ERR_STATE: return "block not held, out of range, or cached under another prefix";
   }
   return "unknown status";
 }

@@ -26,7 +26,9 @@ Readings (the pages are silent; listed in the design doc):
 * a block becomes matchable when its sequence commits it: only full blocks,
   after their K/V have been written;
 * committing a block whose identity is already cached keeps the cached block;
-  the duplicate stays unregistered and is freed when released;
+  the duplicate stays unregistered and is freed when released, and the
+  sequence's later blocks are not registered either (they would follow a block
+  the sequence does not hold);
 * allocation takes the lowest-numbered free block; when none is free it reuses
   the least recently released unreferenced cached block, whose identity is
   dropped; allocation is all or nothing;
@@ -102,14 +104,29 @@ class PrefixCache:
         return out
 
     def commit(self, tokens, block_ids) -> None:
-        """Make the full blocks of a sequence matchable (their K/V are written)."""
+        """Make the full blocks of a sequence matchable (their K/V are written).
+
+        Registration follows the sequence's own chain: at the first block whose
+        prefix is already cached in another block (a duplicate computed cold),
+        it stops, so no registered block ever follows a block its sequence
+        does not hold."""
         tokens = list(tokens)
-        for i in range(min(len(tokens) // self.bs, len(block_ids))):
+        n = min(len(tokens) // self.bs, len(block_ids))
+        if len(set(block_ids[:n])) < n:
+            raise ValueError("a block listed twice")
+        for i in range(n):
             blk = block_ids[i]
             if self.ref[blk] <= 0:
                 raise ValueError("committing a block the sequence does not hold")
             key = tuple(tokens[: self.bs * (i + 1)])
-            if key in self.cached or blk in self.key_of:
+            if blk in self.key_of and self.key_of[blk] != key:
+                raise ValueError("block already cached under another prefix")
+        for i in range(n):
+            blk = block_ids[i]
+            key = tuple(tokens[: self.bs * (i + 1)])
+            if key in self.cached:
+                if self.cached[key] != blk:
+                    return
                 continue
             self.cached[key] = blk
             self.key_of[blk] = key

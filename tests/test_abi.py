@@ -1,5 +1,5 @@
 """C-ABI checks that need no GPU: the library loads, exports every symbol that
-include/kvc.h declares, its host-only functions give the pages' numbers, and bad
+include/*.h declare, its host-only functions give the pages' numbers, and bad
 arguments are rejected before any launch (no call here reaches a kernel)."""
 import ctypes
 import json
@@ -10,22 +10,25 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kvc.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 kvc = pytest.importorskip("kv_cache_decode_append_amd")
 LIB = kvc.LIB
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvc_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(kvc_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert {"kvc_kv_append", "kvc_paged_decode_attention", "kvc_chunked_prefill_attention",
-            "kvc_slot_mapping"} <= set(names)
+            "kvc_slot_mapping", "kvc_prefix_cache_match", "kvc_prefix_cache_commit"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", kvc.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (kvc_[a-z0-9_]+)", out))

@@ -143,6 +143,13 @@ def pin_commit_keeps_the_first_copy(cls=PrefixCache):
     assert pc.n_cached() == 2 and set(pc.key_of) == set(b1)
     pc.release(b2)
     assert set(b2) <= pc.free
+    # a sequence computed cold over the same opening: its duplicate first block
+    # stops registration, so its third block does not become matchable
+    c = a + list(range(100, 116))
+    b3 = pc.allocate(3)
+    pc.commit(c, b3)
+    assert pc.n_cached() == 2
+    assert len(pc.match(c + [0])) == 2
 
 
 def pin_no_mixing_of_cached_prompts(cls=PrefixCache):

@@ -26,6 +26,12 @@ Workloads (shapes taken from the pages' workloads):
   mattered").
 * ``C5`` long context: 8 sequences at 32,000 tokens decode, plus a 2,048-token
   prefill chunk per sequence over a 30,000-token cached prefix.
+* ``P1`` prefix caching, C3's attention shape: a 2,000-token prompt whose first
+  1,800 tokens (system instructions and examples) are shared with a cached
+  prompt (daviddominguez.dev, section "A prefix already in the cache can skip
+  its prefill"); ``shared_prompts`` builds such token lists and
+  ``prefix_values`` gives each position values that depend on its whole token
+  prefix, as a model's keys and values do.
 
 Seeds: workload k draws sequence b's values from ``default_rng([k, b])`` in the
 order K, V (all positions), then Q; the block permutation from
@@ -155,3 +161,43 @@ def small_workload(name: str, wid: int, B: int, Hq: int, Hkv: int, D: int, dtype
                    sigma: float = 1.0) -> Workload:
     """Ad-hoc workload for parity grids (seed namespace ``wid`` >= 100)."""
     return Workload(name, wid, B=B, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, sigma=sigma)
+
+
+P1 = Workload("P1-prefix-bf16", 6, B=1, Hq=32, Hkv=8, D=128, dtype="bf16", sigma=0.5, layers=32)
+P1_PROMPT = 2000
+P1_SHARED = 1800
+PREFIX_VOCAB = 128000
+
+
+def shared_prompts(n_prompts: int, shared: int = P1_SHARED, length: int = P1_PROMPT,
+                   seed: int = 0) -> list[list[int]]:
+    """Token id lists that agree on their first ``shared`` tokens."""
+    rng = np.random.default_rng([P1.wid, 777777, seed])
+    stem = rng.integers(0, PREFIX_VOCAB, shared).tolist()
+    return [stem + rng.integers(0, PREFIX_VOCAB, length - shared).tolist()
+            for _ in range(n_prompts)]
+
+
+def _prefix_seeds(tokens) -> list[int]:
+    """One 63-bit seed per position, a running mix of the tokens up to it."""
+    h, out = 0x2545F4914F6CDD1D, []
+    for t in tokens:
+        h = ((h ^ (int(t) + 0x9E3779B97F4A7C15)) * 0x100000001B3) & ((1 << 64) - 1)
+        out.append(h >> 1)
+    return out
+
+
+def prefix_values(w: Workload, tokens) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """k, v [n, Hkv, D] and q [n, Hq, D] (float32, N(0, 1) * sigma): position p's
+    values are drawn from a generator seeded by tokens[0..p], so two prompts
+    with the same opening have the same values there."""
+    n = len(tokens)
+    k = np.empty((n, w.Hkv, w.D), np.float32)
+    v = np.empty_like(k)
+    q = np.empty((n, w.Hq, w.D), np.float32)
+    for p, sd in enumerate(_prefix_seeds(tokens)):
+        rng = np.random.default_rng([w.wid, sd])
+        k[p] = rng.standard_normal((w.Hkv, w.D), dtype=np.float32) * w.sigma
+        v[p] = rng.standard_normal((w.Hkv, w.D), dtype=np.float32) * w.sigma
+        q[p] = rng.standard_normal((w.Hq, w.D), dtype=np.float32) * w.sigma
+    return k, v, q
