@@ -179,6 +179,37 @@ int kvc_chunked_prefill_attention(const kvc_cache* cache, const void* q, const v
                                   int32_t max_blocks, int32_t Hq, float softmax_scale,
                                   void* out, void* stream);
 
+/* Bytes of workspace kvc_chunked_prefill_attention_split needs for these sizes
+ * (0: no key-range split, no workspace). max_context_len bounds prefix + chunk
+ * over the batch; num_kv_heads is the cache's. 0 for invalid sizes too. */
+size_t kvc_prefill_workspace_bytes(int32_t n_seqs, int32_t total_tokens, int32_t max_chunk_len,
+                                   int32_t max_context_len, int32_t Hq, int32_t num_kv_heads,
+                                   int32_t head_dim);
+
+/* kvc_chunked_prefill_attention for chunks too short to fill the GPU over a
+ * long cached prefix (for example the tokens left after a prefix-cache hit,
+ * daviddominguez.dev, section "A prefix already in the cache can skip its
+ * prefill"): when the query tiles alone give too few workgroups, each one's
+ * keys are split into ranges whose partial softmax states a second kernel
+ * merges on the same stream (the log-sum-exp rule of the split decode).
+ *   max_context_len  host-known bound on prefix + chunk over the batch; a
+ *                    sequence past it sets KVC_DEVERR_CONTEXT (its rows are
+ *                    then incomplete)
+ *   workspace        device scratch of >= kvc_prefill_workspace_bytes(...)
+ *                    bytes, 16-byte aligned, no initialisation needed; may be
+ *                    NULL when that size is 0
+ * Other arguments and outputs as kvc_chunked_prefill_attention; with no split
+ * the two calls run the same kernel and give the same bits.
+ * Returns KVC_ERR_WORKSPACE when the workspace is missing or too small. */
+int kvc_chunked_prefill_attention_split(const kvc_cache* cache, const void* q, const void* k,
+                                        const void* v, int32_t n_seqs,
+                                        const int32_t* cu_chunk_lens, const int32_t* prefix_lens,
+                                        int32_t total_tokens, int32_t max_chunk_len,
+                                        int32_t max_context_len, const int32_t* block_table,
+                                        int32_t max_blocks, int32_t Hq, float softmax_scale,
+                                        void* out, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
 /* Static string for a status code. */
 const char* kvc_status_string(int status);
 

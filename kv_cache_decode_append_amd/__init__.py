@@ -22,5 +22,6 @@ from ._lib import (  # noqa: F401
     kv_append,
     kv_bytes_per_token,
     paged_decode_attention,
+    prefill_workspace_bytes,
     slot_mapping,
 )

@@ -79,6 +79,10 @@ def _load() -> ctypes.CDLL:
                                                 fl, vp, vp, c_sz, vp]),
         "kvc_chunked_prefill_attention": (c_int, [P, vp, vp, vp, c_i32, vp, vp, c_i32, c_i32, vp,
                                                   c_i32, c_i32, fl, vp, vp]),
+        "kvc_prefill_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+        "kvc_chunked_prefill_attention_split": (c_int, [P, vp, vp, vp, c_i32, vp, vp, c_i32, c_i32,
+                                                        c_i32, vp, c_i32, c_i32, fl, vp, vp, c_sz,
+                                                        vp]),
         "kvc_status_string": (ctypes.c_char_p, [c_int]),
         "kvc_prefix_cache_create": (vp, [c_i32, c_i32]),
         "kvc_prefix_cache_destroy": (None, [vp]),
@@ -268,11 +272,22 @@ def decode_append_attention(cache: PagedKVCache, q: torch.Tensor, k_new: torch.T
                    softmax_scale, out, workspace)
 
 
+def prefill_workspace_bytes(n_seqs: int, total_tokens: int, max_chunk_len: int,
+                            max_context_len: int, Hq: int, num_kv_heads: int, head_dim: int) -> int:
+    return int(LIB.kvc_prefill_workspace_bytes(n_seqs, total_tokens, max_chunk_len,
+                                               max_context_len, Hq, num_kv_heads, head_dim))
+
+
 def chunked_prefill_attention(cache: PagedKVCache, q: torch.Tensor, k: torch.Tensor,
                               v: torch.Tensor, cu_chunk_lens: torch.Tensor,
                               prefix_lens: torch.Tensor, block_table: torch.Tensor,
                               max_chunk_len: int, softmax_scale: float | None = None,
-                              out: torch.Tensor | None = None) -> torch.Tensor:
+                              out: torch.Tensor | None = None, max_context_len: int | None = None,
+                              workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """With ``max_context_len`` (a bound on prefix + chunk) the call may split
+    each query tile's keys over several workgroups (kvc_chunked_prefill_attention_split);
+    a workspace of the size the library asks for is allocated here when none
+    is given."""
     dev = cache.k_cache.device
     _need(q, "q", cache.dtype, 3, dev)
     _need(k, "k", cache.dtype, 3, dev)
@@ -290,10 +305,22 @@ def chunked_prefill_attention(cache: PagedKVCache, q: torch.Tensor, k: torch.Ten
         out = torch.empty_like(q)
     _need(out, "out", cache.dtype, 3, dev)
     scale = (1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
-    _check("kvc_chunked_prefill_attention", LIB.kvc_chunked_prefill_attention(
+    if max_context_len is None:
+        _check("kvc_chunked_prefill_attention", LIB.kvc_chunked_prefill_attention(
+            cache.c, q.data_ptr(), k.data_ptr(), v.data_ptr(), n, cu_chunk_lens.data_ptr(),
+            prefix_lens.data_ptr(), total, int(max_chunk_len), block_table.data_ptr(),
+            block_table.shape[1], Hq, scale, out.data_ptr(), _stream()))
+        return out
+    need = prefill_workspace_bytes(n, total, int(max_chunk_len), int(max_context_len), Hq,
+                                   cache.num_kv_heads, D)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("kvc_chunked_prefill_attention_split", LIB.kvc_chunked_prefill_attention_split(
         cache.c, q.data_ptr(), k.data_ptr(), v.data_ptr(), n, cu_chunk_lens.data_ptr(),
-        prefix_lens.data_ptr(), total, int(max_chunk_len), block_table.data_ptr(),
-        block_table.shape[1], Hq, scale, out.data_ptr(), _stream()))
+        prefix_lens.data_ptr(), total, int(max_chunk_len), int(max_context_len),
+        block_table.data_ptr(), block_table.shape[1], Hq, scale, out.data_ptr(),
+        _ptr(workspace), ws_bytes, _stream()))
     return out
 
 

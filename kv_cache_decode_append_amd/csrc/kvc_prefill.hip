@@ -29,6 +29,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "kvc_append.h"
 #include "kvc_device.h"
 #include "kvc_host.h"
@@ -106,8 +108,12 @@ struct PrefillArgs {
   int32_t total;
   int32_t max_chunk;
   int32_t n_qt;       // query tiles per sequence (grid decomposition)
-  int32_t n_work;     // n_qt * hkv * n_seqs
+  int32_t n_split;    // key-range splits per query tile (1: no split, rows written directly)
+  int32_t split_tiles;  // key tiles per split
+  int32_t n_work;     // n_qt * n_split * hkv * n_seqs
   float scale_log2;
+  float* ws_o;        // split partials: [total][Hq][n_split][D] fp32, unnormalised
+  float2* ws_ml;      // [total][Hq][n_split] (running max in log2 units, row sum)
 };
 
 template <typename T>
@@ -138,8 +144,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
   const int work = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (work >= a.n_work) return;
   const int qt = work % a.n_qt;
-  const int kvh = (work / a.n_qt) % a.hkv;
-  const int s = work / (a.n_qt * a.hkv);
+  const int sp = (work / a.n_qt) % a.n_split;
+  const int kvh = (work / (a.n_qt * a.n_split)) % a.hkv;
+  const int s = work / (a.n_qt * a.n_split * a.hkv);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int t0 = a.cu[s];
@@ -147,21 +154,37 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
   const int p0 = a.prefix[s];
   const int pos_lo = qt * S::MP;
   if (!chunk_ok(t0, C, p0, a.total, a.max_chunk)) {
-    if (qt == 0 && kvh == 0 && tid == 0) flag_error(a.err, KVC_DEVERR_CONTEXT);
+    if (qt == 0 && sp == 0 && kvh == 0 && tid == 0) flag_error(a.err, KVC_DEVERR_CONTEXT);
     return;
   }
   if (pos_lo >= C) return;
   const int kv_len = p0 + C;                           // keys that exist after the write
   const int last_pos = p0 + min(pos_lo + S::MP, C) - 1;
-  const int n_tiles = last_pos / kKeyTile + 1;
   const int hq_all = a.hkv * G;
+  // this workgroup's key tiles: [t_begin, t_end) of the ones its rows reach
+  const int t_begin = sp * a.split_tiles;
+  const int t_end = min(last_pos / kKeyTile + 1, t_begin + a.split_tiles);
+  if (sp == a.n_split - 1 && last_pos / kKeyTile + 1 > t_begin + a.split_tiles && tid == 0)
+    flag_error(a.err, KVC_DEVERR_CONTEXT);             // keys past max_context_len
+
+  if (t_begin >= t_end) {
+    // a split past this query tile's keys: an empty partial for each of its rows
+    const int rows = min(S::MP, C - pos_lo) * G;
+    for (int r = tid; r < rows; r += kPfThreads) {
+      const size_t pr = ((size_t)(t0 + pos_lo + r / G) * hq_all + kvh * G + r % G) * a.n_split + sp;
+      a.ws_ml[pr] = float2{-INFINITY, 0.f};
+      for (int d = 0; d < D; d += 4)
+        *reinterpret_cast<f32x4*>(a.ws_o + pr * D + d) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
   const int32_t* bt_row = a.bt + (size_t)s * a.max_blocks;
 
   // The pool row (block id * Hkv + kv head) of every block this workgroup
   // reads, validated once and cached in LDS; -1 for a block that holds no key
   // or has an id outside the pool. Contract violations are collected per lane
   // and flagged once at the end.
-  const int nb_need = (min(kv_len, n_tiles * kKeyTile) + 15) / 16;
+  const int nb_need = (min(kv_len, t_end * kKeyTile) + 15) / 16;
   int bad = 0;
   auto pool_row = [&](int lb) -> int {
     if (lb >= nb_need) return -1;
@@ -176,8 +199,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
     }
     return blk * a.hkv + kvh;
   };
-  for (int i = tid; i < min(4 * (n_tiles + 1), S::BT_CACHE); i += kPfThreads)
-    bt_lds[i] = pool_row(i);
+  const int lb0 = 4 * t_begin;                         // cache entry 0 = block lb0
+  for (int i = tid; i < min(4 * (t_end - t_begin + 1), S::BT_CACHE); i += kPfThreads)
+    bt_lds[i] = pool_row(lb0 + i);
 
   // rows owned by this lane: r = w*32 + n*16 + l16
   int row_pos[kRowTiles];                              // absolute position (clamped)
@@ -220,7 +244,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
   // common path never waits for an outstanding K/V load.
   const __amdgpu_buffer_rsrc_t bt_rsrc = make_rsrc(bt_row, (uint32_t)a.max_blocks * 4u);
   auto block_row = [&](int lb, bool cached) -> int {
-    if (cached) return bt_lds[lb];
+    if (cached) return bt_lds[lb - lb0];
     int r = -1;
     if (lb < nb_need) {
       if (lb >= a.max_blocks) {
@@ -259,7 +283,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
   // of an absent block reads inside the pool's first block (always valid).
   static_assert(16 % (64 / S::NC) == 0, "a wave's K rows stay in one block");
   auto load_k = [&](int kt) {
-    const bool cached = 4 * kt < S::BT_CACHE;
+    const bool cached = 4 * (kt - t_begin) < S::BT_CACHE;
 #pragma unroll
     for (int j = 0; j < S::KPT; ++j) {
       const int ci = tid + j * kPfThreads;
@@ -273,7 +297,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
     }
   };
   auto load_v = [&](int kt) {
-    const bool cached = 4 * kt < S::BT_CACHE;
+    const bool cached = 4 * (kt - t_begin) < S::BT_CACHE;
 #pragma unroll
     for (int j = 0; j < S::VPT; ++j) {
       const int u = tid + j * kPfThreads;
@@ -565,21 +589,21 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
   f32x4 sacc[4][kRowTiles];
   PTile pt;
   float alpha[kRowTiles];
-  load_k(0);
-  load_v(0);
-  store_k(kbuf(0));
-  store_v(vbuf(0));
-  if (n_tiles > 1) {
-    load_k(1);
-    store_k(kbuf(1));
+  load_k(t_begin);
+  load_v(t_begin);
+  store_k(kbuf(t_begin));
+  store_v(vbuf(t_begin));
+  if (t_end - t_begin > 1) {
+    load_k(t_begin + 1);
+    store_k(kbuf(t_begin + 1));
   }
   lds_barrier();
-  qk(kbuf(0), sacc);
-  mask(sacc, 0);
+  qk(kbuf(t_begin), sacc);
+  mask(sacc, t_begin * kKeyTile);
   softmax(sacc, pt, alpha);                           // o is still zero: no rescale
   lds_barrier();                                       // K(0) read by every wave
-  for (int kt = 0; kt + 1 < n_tiles; ++kt) {
-    const bool more_k = kt + 2 < n_tiles;
+  for (int kt = t_begin; kt + 1 < t_end; ++kt) {
+    const bool more_k = kt + 2 < t_end;
     if (more_k) load_k(kt + 2);
     load_v(kt + 1);
     qk(kbuf(kt + 1), sacc);
@@ -605,7 +629,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
     store_v(vbuf(kt + 1));
     lds_barrier();
   }
-  pv(vbuf(n_tiles - 1), pt);
+  pv(vbuf(t_end - 1), pt);
 
   if (bad) flag_error(a.err, bad);
 
@@ -618,10 +642,46 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
     if (!row_ok[n]) continue;
     const int r = w * (kRowTiles * 16) + n * 16 + l16;
     const int pl = pos_lo + r / G, h = r % G;
-    const size_t orow = ((size_t)(t0 + pl) * hq_all + kvh * G + h) * D;
-    const float inv = 1.f / l_row[n];
+    const size_t row = (size_t)(t0 + pl) * hq_all + kvh * G + h;
+    if (a.n_split == 1) {
+      const float inv = 1.f / l_row[n];
 #pragma unroll
-    for (int dt = 0; dt < S::DT; ++dt) store4<T>(a.out, orow + dt * 16 + g * 4, o[n][dt], inv);
+      for (int dt = 0; dt < S::DT; ++dt) store4<T>(a.out, row * D + dt * 16 + g * 4, o[n][dt], inv);
+    } else {
+      // partial of this key range: unnormalised accumulators, running max, row sum
+      const size_t pr = row * a.n_split + sp;
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt)
+        *reinterpret_cast<f32x4*>(a.ws_o + pr * D + dt * 16 + g * 4) = o[n][dt];
+      if (g == 0) a.ws_ml[pr] = float2{m_run[n], l_row[n]};
+    }
+  }
+}
+
+// One wave per (token, query head): combine the key-range partials of a split
+// prefill with the log-sum-exp rule (the same rule the split decode uses).
+template <typename T, int D>
+__global__ __launch_bounds__(64) void prefill_merge_kernel(PrefillArgs a, int32_t hq_all) {
+  const size_t row = blockIdx.x;                       // token * Hq + head
+  if (row >= (size_t)a.total * hq_all) return;
+  const float2* ml = a.ws_ml + row * a.n_split;
+  float M = -INFINITY;
+  for (int i = 0; i < a.n_split; ++i) M = fmaxf(M, ml[i].x);
+  float L = 0.f;
+  for (int i = 0; i < a.n_split; ++i)
+    if (ml[i].x != -INFINITY) L += ml[i].y * __builtin_amdgcn_exp2f(ml[i].x - M);
+  const float inv = 1.f / L;
+  for (int d = threadIdx.x; d < D; d += 64) {
+    float acc = 0.f;
+    for (int i = 0; i < a.n_split; ++i)
+      if (ml[i].x != -INFINITY)
+        acc += __builtin_amdgcn_exp2f(ml[i].x - M) * a.ws_o[(row * a.n_split + i) * D + d];
+    const float v = acc * inv;
+    if constexpr (ElemBytes<T>::value == 4) {
+      reinterpret_cast<float*>(a.out)[row * D + d] = v;
+    } else {
+      reinterpret_cast<uint16_t*>(a.out)[row * D + d] = (uint16_t)f32_to_bf16_bits(v);
+    }
   }
 }
 
@@ -629,9 +689,14 @@ template <typename T, int D, int G>
 int launch_prefill(PrefillArgs a, int n_seqs, int max_chunk, hipStream_t st) {
   using S = PfShape<T, D, G>;
   a.n_qt = (max_chunk + S::MP - 1) / S::MP;
-  a.n_work = a.n_qt * a.hkv * n_seqs;
+  a.n_work = a.n_qt * a.n_split * a.hkv * n_seqs;
   const int grid = (a.n_work + 7) / 8 * 8;           // whole XCD rounds
   hipLaunchKernelGGL((prefill_attention_kernel<T, D, G>), dim3(grid), dim3(kPfThreads), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return KVC_ERR_LAUNCH;
+  if (a.n_split > 1) {
+    hipLaunchKernelGGL((prefill_merge_kernel<T, D>), dim3((unsigned)a.total * a.hkv * G), dim3(64), 0,
+                       st, a, a.hkv * G);
+  }
   return launch_status();
 }
 
@@ -664,15 +729,44 @@ int dispatch_prefill(const PrefillArgs& a, int dtype, int D, int G, int n, int m
   return KVC_ERR_UNSUPPORTED;
 }
 
-}  // namespace kvc
+// Key-range splits: when the query tiles alone give fewer than kPfTargetWork
+// workgroups (a short chunk over a long cached prefix, such as the part of a
+// prompt left after a prefix-cache hit), each query tile's keys are split into
+// ranges of at least kPfMinSplitTiles tiles, and a merge combines the partials.
+constexpr int kPfTargetWork = 512;
+constexpr int kPfMinSplitTiles = 4;
+constexpr int kPfMaxSplit = 32;
 
-extern "C" int kvc_chunked_prefill_attention(const kvc_cache* cache, const void* q, const void* k,
-                                             const void* v, int32_t n_seqs, const int32_t* cu_chunk_lens,
-                                             const int32_t* prefix_lens, int32_t total_tokens,
-                                             int32_t max_chunk_len, const int32_t* block_table,
-                                             int32_t max_blocks, int32_t Hq, float softmax_scale,
-                                             void* out, void* stream) {
-  int st = kvc::check_cache(cache);
+struct PfSplit {
+  int n_split;
+  int split_tiles;
+};
+
+PfSplit prefill_split(int n_seqs, int max_chunk, int max_ctx, int hkv, int G) {
+  const int64_t n_qt = ceil_div(max_chunk, kRows / G);
+  const int64_t base = n_qt * hkv * n_seqs;
+  const int max_tiles = (int)ceil_div(max_ctx, kKeyTile);
+  int n = 1;
+  if (max_ctx > 0 && base < kPfTargetWork)
+    n = (int)std::min<int64_t>(ceil_div(kPfTargetWork, base), max_tiles / kPfMinSplitTiles);
+  n = std::max(1, std::min(n, kPfMaxSplit));
+  if (n == 1) return {1, 1 << 30};
+  const int tiles = (int)ceil_div(max_tiles, n);
+  return {(int)ceil_div(max_tiles, tiles), tiles};
+}
+
+size_t prefill_ws_bytes(const PfSplit& sp, int total, int Hq, int D) {
+  if (sp.n_split <= 1) return 0;
+  return (size_t)total * Hq * sp.n_split * ((size_t)D * 4 + 8);
+}
+
+static int prefill_entry(const kvc_cache* cache, const void* q, const void* k, const void* v,
+                         int32_t n_seqs, const int32_t* cu_chunk_lens, const int32_t* prefix_lens,
+                         int32_t total_tokens, int32_t max_chunk_len, int32_t max_context_len,
+                         const int32_t* block_table, int32_t max_blocks, int32_t Hq,
+                         float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  int st = check_cache(cache);
   if (st != KVC_OK) return st;
   if (n_seqs < 0 || total_tokens < 0 || max_chunk_len < 0 || max_blocks < 0 || Hq <= 0)
     return KVC_ERR_SHAPE;
@@ -682,11 +776,18 @@ extern "C" int kvc_chunked_prefill_attention(const kvc_cache* cache, const void*
   if (n_seqs == 0 || total_tokens == 0 || max_chunk_len == 0) return KVC_OK;
   if (cache->num_blocks < 1) return KVC_ERR_SHAPE;   // a chunk needs somewhere to go
   if (!q || !k || !v || !cu_chunk_lens || !prefix_lens || !block_table || !out) return KVC_ERR_NULL;
-  hipStream_t s = kvc::as_stream(stream);
-  st = kvc::launch_chunk_append(cache, k, v, n_seqs, cu_chunk_lens, prefix_lens, total_tokens,
-                                max_chunk_len, block_table, max_blocks, s);
+  PfSplit sp{1, 1 << 30};
+  if (max_context_len >= 0) {
+    if (max_context_len < max_chunk_len) return KVC_ERR_SHAPE;
+    sp = prefill_split(n_seqs, max_chunk_len, max_context_len, cache->num_kv_heads, G);
+  }
+  const size_t need = prefill_ws_bytes(sp, total_tokens, Hq, cache->head_dim);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KVC_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  st = launch_chunk_append(cache, k, v, n_seqs, cu_chunk_lens, prefix_lens, total_tokens,
+                           max_chunk_len, block_table, max_blocks, s);
   if (st != KVC_OK) return st;
-  kvc::PrefillArgs a;
+  PrefillArgs a;
   a.q = q;
   a.kc = cache->k_cache;
   a.vc = cache->v_cache;
@@ -700,6 +801,49 @@ extern "C" int kvc_chunked_prefill_attention(const kvc_cache* cache, const void*
   a.max_blocks = max_blocks;
   a.total = total_tokens;
   a.max_chunk = max_chunk_len;
+  a.n_split = sp.n_split;
+  a.split_tiles = sp.split_tiles;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  return kvc::dispatch_prefill(a, cache->dtype, cache->head_dim, G, n_seqs, max_chunk_len, s);
+  a.ws_o = reinterpret_cast<float*>(workspace);
+  a.ws_ml = need > 0 ? reinterpret_cast<float2*>(reinterpret_cast<uint8_t*>(workspace) +
+                                                  (size_t)total_tokens * Hq * sp.n_split *
+                                                      cache->head_dim * 4)
+                     : nullptr;
+  return dispatch_prefill(a, cache->dtype, cache->head_dim, G, n_seqs, max_chunk_len, s);
+}
+
+}  // namespace kvc
+
+extern "C" size_t kvc_prefill_workspace_bytes(int32_t n_seqs, int32_t total_tokens,
+                                              int32_t max_chunk_len, int32_t max_context_len,
+                                              int32_t Hq, int32_t num_kv_heads, int32_t head_dim) {
+  if (n_seqs <= 0 || total_tokens <= 0 || max_chunk_len <= 0 || max_context_len < max_chunk_len ||
+      Hq <= 0 || num_kv_heads <= 0 || head_dim <= 0 || Hq % num_kv_heads != 0)
+    return 0;
+  const kvc::PfSplit sp =
+      kvc::prefill_split(n_seqs, max_chunk_len, max_context_len, num_kv_heads, Hq / num_kv_heads);
+  return kvc::prefill_ws_bytes(sp, total_tokens, Hq, head_dim);
+}
+
+extern "C" int kvc_chunked_prefill_attention_split(
+    const kvc_cache* cache, const void* q, const void* k, const void* v, int32_t n_seqs,
+    const int32_t* cu_chunk_lens, const int32_t* prefix_lens, int32_t total_tokens,
+    int32_t max_chunk_len, int32_t max_context_len, const int32_t* block_table, int32_t max_blocks,
+    int32_t Hq, float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (max_context_len < 0) return KVC_ERR_SHAPE;
+  return kvc::prefill_entry(cache, q, k, v, n_seqs, cu_chunk_lens, prefix_lens, total_tokens,
+                            max_chunk_len, max_context_len, block_table, max_blocks, Hq,
+                            softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int kvc_chunked_prefill_attention(const kvc_cache* cache, const void* q, const void* k,
+                                             const void* v, int32_t n_seqs, const int32_t* cu_chunk_lens,
+                                             const int32_t* prefix_lens, int32_t total_tokens,
+                                             int32_t max_chunk_len, const int32_t* block_table,
+                                             int32_t max_blocks, int32_t Hq, float softmax_scale,
+                                             void* out, void* stream) {
+  return kvc::prefill_entry(cache, q, k, v, n_seqs, cu_chunk_lens, prefix_lens, total_tokens,
+                            max_chunk_len, -1, block_table, max_blocks, Hq, softmax_scale, out,
+                            nullptr, 0, stream);
 }

@@ -200,9 +200,10 @@ class PrefillCase:
             OP.scatter(pv, slots, oracle_bits(self.v[i], self.w.dtype))
         return pk, pv
 
-    def run_gpu(self, kvc, cache=None):
+    def run_gpu(self, kvc, cache=None, max_context_len=None):
         """Cache the prefixes through slot_mapping + kv_append, then one chunked
-        prefill call for all sequences. Returns (cache, out [sum C, Hq, D])."""
+        prefill call for all sequences (the key-range split entry point when
+        max_context_len is given). Returns (cache, out [sum C, Hq, D])."""
         w, dev = self.w, "cuda"
         if cache is None:
             cache = kvc.PagedKVCache.allocate(self.num_blocks, w.Hkv, w.D, TDTYPE[w.dtype],
@@ -224,7 +225,8 @@ class PrefillCase:
         v = to_device(np.concatenate([self.v[i][self.prefix[i]:] for i in range(self.n)]), w.dtype)
         out = kvc.chunked_prefill_attention(
             cache, q, k, v, torch.from_numpy(cu).to(dev),
-            torch.from_numpy(self.prefix.astype(np.int32)).to(dev), bt, int(self.chunk.max()))
+            torch.from_numpy(self.prefix.astype(np.int32)).to(dev), bt, int(self.chunk.max()),
+            max_context_len=max_context_len)
         torch.cuda.synchronize()
         self.cu = cu
         return cache, out

@@ -98,6 +98,26 @@ def test_bad_shapes_rejected_before_launch():
     assert LIB.kvc_slot_mapping(1, 1, 4, 8, 1, 1, -5, 16, 1, None, None) == -2
 
 
+def test_prefill_split_workspace_rules():
+    # 208 query tokens over a 2,000-token context, GQA 32/8/128: 8 key-range splits
+    assert kvc.prefill_workspace_bytes(1, 208, 208, 2000, 32, 8, 128) == 208 * 32 * 8 * (128 * 4 + 8)
+    # enough query tiles already (8 x 2,048 tokens): no split, no workspace
+    assert kvc.prefill_workspace_bytes(8, 16384, 2048, 32048, 32, 8, 128) == 0
+    assert kvc.prefill_workspace_bytes(1, 208, 208, 100, 32, 8, 128) == 0   # context < chunk
+    c = _cache(num_kv_heads=2, head_dim=64)
+    byref = ctypes.byref(c)
+    args = (byref, 1, 1, 1, 1, 1, 1, 208, 208)
+    tail = (1, 200, 8, 0.125, 1)
+    # split needed, workspace missing or one byte short
+    need = kvc.prefill_workspace_bytes(1, 208, 208, 2000, 8, 2, 64)
+    assert need > 0
+    assert LIB.kvc_chunked_prefill_attention_split(*args, 2000, *tail, None, 0, None) == -5
+    assert LIB.kvc_chunked_prefill_attention_split(*args, 2000, *tail, 1, need - 1, None) == -5
+    # the context bound below the chunk, or negative
+    assert LIB.kvc_chunked_prefill_attention_split(*args, 100, *tail, 1, need, None) == -2
+    assert LIB.kvc_chunked_prefill_attention_split(*args, -1, *tail, 1, need, None) == -2
+
+
 def test_zero_sized_calls_launch_nothing():
     c = _cache()
     assert LIB.kvc_kv_append(ctypes.byref(c), 1, 1, 1, 0, None) == 0
@@ -107,6 +127,6 @@ def test_zero_sized_calls_launch_nothing():
 
 
 def test_status_strings():
-    for s in range(-6, 1):
+    for s in range(-8, 1):
         assert LIB.kvc_status_string(s)
     assert LIB.kvc_status_string(-99) == b"unknown status"

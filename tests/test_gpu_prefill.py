@@ -15,8 +15,8 @@ def kvc():
     return m
 
 
-def _check(kvc, case: PrefillCase, what: str, pool=True, rows=None):
-    cache, out = case.run_gpu(kvc)
+def _check(kvc, case: PrefillCase, what: str, pool=True, rows=None, max_context_len=None):
+    cache, out = case.run_gpu(kvc, max_context_len=max_context_len)
     assert int(cache.err_flag.item()) == 0
     if pool:
         pk, pv = case.oracle_pool()
@@ -116,3 +116,43 @@ def test_c5_prefill_chunk_over_long_prefix(kvc):
         for p in [W.C5_PREFIX, W.C5_PREFIX + 1, W.C5_PREFIX + 2047]:
             s = OP.slot_of(case.bt[i], p, 16)
             assert np.array_equal(kb[s // 16, :, s % 16, :], oracle_bits(case.k[i][p], "bf16"))
+
+
+@pytest.mark.parametrize("dtype,d,g", [("bf16", 128, 4), ("bf16", 64, 8), ("bf16", 32, 1),
+                                       ("fp32", 64, 2), ("fp32", 128, 4)])
+def test_split_keys_short_chunks_over_long_prefixes(kvc, dtype, d, g):
+    """Few query tiles over long prefixes: the split entry point spreads each
+    query tile's keys over several workgroups and merges them. The 700-token
+    chunk over no prefix has query tiles whose keys end before the later
+    splits start (empty partials)."""
+    w = W.small_workload(f"pf-split-{dtype}-{d}-{g}", 970 + g * 100 + d, B=4, Hq=2 * g, Hkv=2,
+                         D=d, dtype=dtype, sigma=0.5 if dtype == "bf16" else 1.0)
+    prefix = [1900, 3000, 0, 257]
+    chunk = [100, 7, 700, 64]
+    max_ctx = max(p + c for p, c in zip(prefix, chunk))
+    need = kvc.prefill_workspace_bytes(4, sum(chunk), max(chunk), max_ctx, w.Hq, w.Hkv, d)
+    assert need > 0, "this case is meant to split"
+    say(f"prefill split {dtype} D={d} G={g}: workspace {need} B")
+    case = PrefillCase(w, prefix, chunk, 400)
+    _check(kvc, case, f"split {dtype} D={d} G={g}", max_context_len=max_ctx)
+
+
+def test_split_entry_without_split_is_the_same_kernel(kvc):
+    """C5-sized work needs no split: the split entry point gives the plain call's bits."""
+    say("prefill split entry, no split needed: bitwise equal to the plain call")
+    w = W.small_workload("pf-nosplit", 985, B=8, Hq=32, Hkv=8, D=128, dtype="bf16", sigma=0.5)
+    case = PrefillCase(w, [500] * 8, [512] * 8, 8 * 64)
+    assert kvc.prefill_workspace_bytes(8, 8 * 512, 512, 1012, 32, 8, 128) == 0
+    _, plain = case.run_gpu(kvc)
+    _, split = case.run_gpu(kvc, max_context_len=1012)
+    assert torch.equal(plain, split)
+
+
+def test_split_context_bound_too_small_is_flagged(kvc):
+    """A sequence longer than max_context_len: the rows miss keys, and the
+    device flag says so (no access outside the pool either way)."""
+    say("prefill split with max_context_len below a sequence's length")
+    w = W.small_workload("pf-split-bad", 986, B=1, Hq=8, Hkv=2, D=64, dtype="bf16", sigma=0.5)
+    case = PrefillCase(w, [3000], [7], 300)
+    cache, _ = case.run_gpu(kvc, max_context_len=1000)
+    assert int(cache.err_flag.item()) & kvc.DEVERR_CONTEXT

@@ -99,6 +99,23 @@ def test_warm_prefill_over_shared_blocks(kvc):
                             oracle_values(vB[:p + 1], "bf16"), scale)
         assert_close(got[r], ref, "bf16", f"warm prefill row {p}")
 
+    # the same warm prefill through the key-range split (8 splits of 4 tiles)
+    out_split = kvc.chunked_prefill_attention(
+        cache, to_device(qB[start:n], "bf16"), to_device(kB[start:n], "bf16"),
+        to_device(vB[start:n], "bf16"), torch.tensor([0, n - start], dtype=torch.int32).cuda(),
+        torch.tensor([start], dtype=torch.int32).cuda(),
+        torch.tensor([bb + [-1] * (maxb - len(bb))], dtype=torch.int32).cuda(), n - start,
+        max_context_len=n)
+    torch.cuda.synchronize()
+    assert int(cache.err_flag.item()) == 0
+    got_s = out_split.float().cpu().numpy()
+    assert_close(got_s, out_warm.float().cpu().numpy(), "bf16", "split vs unsplit warm prefill")
+    for r in [0, 100, n - start - 1]:
+        p = start + r
+        ref = OA.attend_row(oracle_values(qB[p], "bf16"), oracle_values(kB[:p + 1], "bf16"),
+                            oracle_values(vB[:p + 1], "bf16"), scale)
+        assert_close(got_s[r], ref, "bf16", f"split warm prefill row {p}")
+
     # one decode step of B over the shared blocks and over the unshared copy
     more = pc.allocate(2)
     d_shared = _decode(kvc, cache, qB[n], kB[n], vB[n], n + 1, bb + more[:1], maxb)
