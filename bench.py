@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--workload", default="c3-decode",
-                    choices=["c3-decode", "c5-decode", "c5-prefill", "prefix-warm"])
+                    choices=["c3-decode", "c4-mixed", "c5-decode", "c5-prefill", "prefix-warm"])
     return ap.parse_args()
 
 
@@ -146,6 +146,8 @@ def main():
         return bench_c5_prefill(args)
     if args.workload == "prefix-warm":
         return bench_prefix_warm(args)
+    if args.workload == "c4-mixed":
+        return bench_c4_mixed(args)
 
     import torch
 
@@ -371,6 +373,90 @@ def bench_c5_prefill(args):
                       "frac": round(tf / 2500.0, 4), "traffic": None,
                       "avg_us": round(ms * 1e3, 1), "flop_per_launch": flop})
     res["steps"] = steps
+    print(json.dumps(res), flush=True)
+
+
+def bench_c4_mixed(args):
+    """The skewed continuous-batching step: 210 sequences with lognormal context
+    lengths (median 6,000, tail clipped at 32,000); 206 decode one token each
+    (one fused append + attention launch, split over partitions for the long
+    ones) and 4 run a 2,048-token prefill chunk over their prefix (one launch).
+    One layer's pool (~6.5 GB, far larger than the caches) is timed per step
+    and reported per layer and for 32 layers."""
+    import torch
+
+    import kv_cache_decode_append_amd as kvc
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = W.C4
+    Hq, Hkv, D, L = w.Hq, w.Hkv, w.D, 32
+    ctx = W.context_lengths(w)
+    pre_rows = W.c4_prefill_rows(ctx)
+    dec_rows = np.array([b for b in range(w.B) if b not in set(pre_rows.tolist())])
+    need = int(sum(W.blocks_for(int(c)) for c in ctx))
+    nb = need + need // 100
+    bt_all = torch.from_numpy(W.block_tables(w, ctx, nb)).to(dev)
+    cache = kvc.PagedKVCache.allocate(nb, Hkv, D, torch.bfloat16, device=dev)
+    cache.k_cache.normal_(0, 0.5)
+    cache.v_cache.normal_(0, 0.5)
+    nd, chunk = len(dec_rows), W.C4_CHUNK
+    q_dec = torch.empty(nd, Hq, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
+    k_dec = torch.empty(nd, Hkv, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
+    v_dec = torch.empty_like(k_dec).normal_(0, 0.5)
+    bt_dec = bt_all.index_select(0, torch.from_numpy(dec_rows.astype(np.int64)).to(dev)).contiguous()
+    ctx_dec = torch.from_numpy(ctx[dec_rows].astype(np.int32)).to(dev)
+    max_dec = int(ctx[dec_rows].max())
+    ws = torch.empty(max(1, kvc.decode_workspace_bytes(nd, Hq, D, max_dec)), dtype=torch.uint8,
+                     device=dev)
+    out_dec = torch.empty_like(q_dec)
+    npre = len(pre_rows)
+    q_pre = torch.empty(npre * chunk, Hq, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
+    k_pre = torch.empty(npre * chunk, Hkv, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
+    v_pre = torch.empty_like(k_pre).normal_(0, 0.5)
+    out_pre = torch.empty_like(q_pre)
+    cu = torch.arange(0, (npre + 1) * chunk, chunk, dtype=torch.int32, device=dev)
+    prefix = torch.from_numpy((ctx[pre_rows] - chunk).astype(np.int32)).to(dev)
+    bt_pre = bt_all.index_select(0, torch.from_numpy(pre_rows.astype(np.int64)).to(dev)).contiguous()
+
+    def dec(i):
+        kvc.decode_append_attention(cache, q_dec, k_dec, v_dec, bt_dec, ctx_dec, max_dec,
+                                    out=out_dec, workspace=ws)
+
+    def pre(i):
+        kvc.chunked_prefill_attention(cache, q_pre, k_pre, v_pre, cu, prefix, bt_pre, chunk,
+                                      out=out_pre)
+
+    def step(i):
+        dec(i)
+        pre(i)
+
+    ms_dec = _timed(dec, args.steps, args.warmup)
+    ms_pre = _timed(pre, max(1, args.steps // 4), max(1, args.warmup // 4))
+    ms_step = _timed(step, max(1, args.steps // 4), max(1, args.warmup // 4))
+    assert int(cache.err_flag.item()) == 0
+    kv_dec = int(ctx[dec_rows].sum()) * Hkv * D * 2 * 2
+    pairs = sum(Hq * (chunk * (int(c) - chunk) + chunk * (chunk + 1) // 2) for c in ctx[pre_rows])
+    flop = pairs * 4 * D
+    gbs = kv_dec / (ms_dec * 1e-3) / 1e9
+    tf = flop / (ms_pre * 1e-3) / 1e12
+    res = _base_line(args, "skewed mixed step (206 decode rows + 4 prefill chunks): decode KV-read "
+                     "GB/s", round(gbs, 1), "GB/s", ms_step, "bf16",
+                     {"workload": "210 sequences, lognormal context (median 6,000, clipped at "
+                                  "32,000), 206 decode + 4 x 2,048-token prefill chunks, GQA "
+                                  "32/8, head_dim 128, bf16, one layer timed",
+                      "B": int(w.B), "ctx_sum": int(ctx.sum()), "ctx_max": int(ctx.max()),
+                      "prefill_rows": pre_rows.tolist(), "pool_blocks": nb},
+                     {"bound": "hbm", "kernel": "paged_decode_kernel + decode_merge_kernel",
+                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                      "avg_us": round(ms_dec * 1e3, 2), "bytes_per_launch": kv_dec})
+    res["decode_ms_per_layer"] = round(ms_dec, 4)
+    res["prefill_ms_per_layer"] = round(ms_pre, 4)
+    res["step_ms_per_layer"] = round(ms_step, 4)
+    res["step_ms_32_layers"] = round(ms_step * L, 3)
+    res["prefill_tflops"] = round(tf, 1)
+    res["prefill_mfma_frac"] = round(tf / 2500.0, 4)
     print(json.dumps(res), flush=True)
 
 

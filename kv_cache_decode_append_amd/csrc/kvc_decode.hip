@@ -86,6 +86,7 @@ struct DecodeArgs {
   float2* ws_ml;      // [B*Hq][n_part]
   int32_t* err;
   int32_t hkv;
+  int32_t n_seqs;     // B
   int32_t num_blocks;
   int32_t max_blocks;
   int32_t max_ctx;
@@ -155,7 +156,14 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
   using S = DecodeShape<T, D, G>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
 
-  const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // One-dimensional grid, kv head fastest, then sequence, partition slowest:
+  // workgroups are dealt round-robin to the 8 XCDs by linear index, so every
+  // partition level spreads over all of them. (With the partition fastest, a
+  // batch whose sequences mostly need one or two partitions put nearly all
+  // the work on one or two XCDs.)
+  const int kvh = blockIdx.x % a.hkv;
+  const int b = (blockIdx.x / a.hkv) % a.n_seqs;
+  const int part = blockIdx.x / (a.n_seqs * a.hkv);
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform across the wave; saying so keeps every buffer
   // descriptor and loop bound in scalar registers (no per-lane waterfall)
@@ -490,7 +498,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int32_t 
 
 template <typename T, int D, int G>
 int launch_decode(const DecodeArgs& a, int B, hipStream_t st) {
-  hipLaunchKernelGGL((paged_decode_kernel<T, D, G>), dim3(a.n_part, a.hkv, B), dim3(kWaves * 64), 0, st, a);
+  hipLaunchKernelGGL((paged_decode_kernel<T, D, G>), dim3((unsigned)(a.n_part * a.hkv * B)),
+                     dim3(kWaves * 64), 0, st, a);
   if (hipGetLastError() != hipSuccess) return KVC_ERR_LAUNCH;
   if (a.n_part > 1) {
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(B * a.hkv * G), dim3(64), 0, st, a, a.hkv * G);
@@ -602,6 +611,7 @@ static int decode_entry(const kvc_cache* cache, const void* q, const void* k_new
                  : nullptr;
   a.err = cache->err_flag;
   a.hkv = cache->num_kv_heads;
+  a.n_seqs = B;
   a.num_blocks = cache->num_blocks;
   a.max_blocks = max_blocks;
   a.max_ctx = max_context_len;
