@@ -16,9 +16,11 @@ Everything here is plain, slow and meant to be read against the pages:
 * ``sizes``: KV bytes per token and the capacity arithmetic.
 * ``prefix``: prefix caching, i.e. whole-block matching of a prompt's opening
   tokens against cached blocks, with reference counts and block reuse.
+* ``sched``: iteration-level scheduling of a request queue (continuous
+  batching under decode-first or prefill-first steps, static batching).
 
 Every function is pinned by a CPU test (``tests/test_oracle_*.py``) against
 values the pages print, closed forms, special cases, library routines or
 brute force; see each function's docstring for its pin.
 """
-from . import attention, bf16, paged, prefix, sizes  # noqa: F401
+from . import attention, bf16, paged, prefix, sched, sizes  # noqa: F401
