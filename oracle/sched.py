@@ -124,3 +124,64 @@ def first_token_and_finish_steps(steps, n: int):
         for r in st.finished:
             fin[r] = i
     return first, fin
+
+
+def _blocks_for(tokens: int, block_size: int) -> int:
+    return (tokens + block_size - 1) // block_size
+
+
+def step_batches(steps, prompts, answers, num_blocks: int, block_size: int = 16) -> list:
+    """The kernel inputs of each step: which cache blocks each row reads and
+    writes.
+
+    A request holds the blocks its tokens occupy: before a step runs, each row
+    of the step (decode rows first, then prefill chunks, each in the order the
+    step lists them) takes the lowest-numbered free blocks until it holds
+    ceil(tokens / block_size) of them, counting the tokens the step writes;
+    after the step, every request that leaves returns all of its blocks (the
+    paged layout of the aiwithghost page's memory section; block order and
+    timing are readings). A decode row of a request with a prompt of p tokens
+    and g tokens generated so far writes the K/V of its newest token at
+    position p + g - 1 and attends over p + g positions.
+
+    Returns, per step, ``{"decode": [(id, context_len, blocks)], "prefill":
+    [(id, start, take, blocks)]}`` with ``blocks`` the request's block list
+    after the step's allocation. Raises ``MemoryError`` when the pool runs out.
+    """
+    n = len(prompts)
+    free = set(range(num_blocks))
+    held = [[] for _ in range(n)]
+    covered = [0] * n
+    gen = [0] * n
+    out = []
+
+    def grow(r, tokens):
+        need = _blocks_for(tokens, block_size) - len(held[r])
+        if need > len(free):
+            raise MemoryError("KV block pool exhausted")
+        for _ in range(max(0, need)):
+            b = min(free)
+            free.remove(b)
+            held[r].append(b)
+
+    for st in steps:
+        dec, pf = [], []
+        for r in st.decode:
+            ctx = prompts[r] + gen[r]
+            grow(r, ctx)
+            dec.append((r, ctx, list(held[r])))
+        for r, start, take in st.prefill:
+            assert start == covered[r]
+            grow(r, start + take)
+            pf.append((r, start, take, list(held[r])))
+        for r, start, take in st.prefill:
+            covered[r] += take
+        for r in st.first_token:
+            gen[r] = 1
+        for r in st.decode:
+            gen[r] += 1
+        for r in st.finished:
+            free.update(held[r])
+            held[r] = []
+        out.append({"decode": dec, "prefill": pf})
+    return out
