@@ -63,9 +63,10 @@ enum {
   KVC_ERR_UNSUPPORTED = -4, /* head_dim / block_size / G outside the supported set */
   KVC_ERR_WORKSPACE = -5,   /* workspace missing or smaller than the size query */
   KVC_ERR_LAUNCH = -6,      /* the HIP runtime rejected a launch */
-  KVC_ERR_NO_BLOCKS = -7,   /* prefix cache: not enough free or reusable blocks */
-  KVC_ERR_STATE = -8        /* prefix cache: a block released or committed that the
+  KVC_ERR_NO_BLOCKS = -7,   /* prefix cache, scheduler: not enough free or reusable blocks */
+  KVC_ERR_STATE = -8,       /* prefix cache: a block released or committed that the
                                caller does not hold, or out of range */
+  KVC_ERR_NO_MEMORY = -9    /* host memory ran out (prefix cache, scheduler) */
 };
 
 /* Bits OR-ed into cache->err_flag by kernels that skipped an invalid access. */

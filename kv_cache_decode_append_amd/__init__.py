@@ -1,7 +1,8 @@
 """Paged KV-cache append, GQA decode attention and chunked-prefill attention on
 AMD MI355X (gfx950): HIP kernels behind the C ABI in include/kvc.h, with this
 thin binding on top, and a host-side prefix-caching block manager
-(include/kvc_prefix.h). Importing the package loads libkvc.so and raises if it is
+(include/kvc_prefix.h), and an iteration-level scheduler that builds each
+step's batch descriptors (include/kvc_sched.h). Importing the package loads libkvc.so and raises if it is
 missing; there is no CPU fallback.
 """
 from ._lib import (  # noqa: F401
@@ -16,6 +17,11 @@ from ._lib import (  # noqa: F401
     KvcError,
     PagedKVCache,
     PrefixCache,
+    SCHED_DECODE_FIRST,
+    SCHED_PREFILL_FIRST,
+    SCHED_STATIC,
+    SchedStep,
+    Scheduler,
     chunked_prefill_attention,
     decode_append_attention,
     decode_workspace_bytes,

@@ -9,8 +9,10 @@ loaded, importing this module raises.
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +42,19 @@ class _CCache(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("err_flag", ctypes.c_void_p),
     ]
+
+
+class _CStep(ctypes.Structure):
+    """kvc_step (include/kvc_sched.h)."""
+    _p = ctypes.POINTER(ctypes.c_int32)
+    _fields_ = [("n_decode", ctypes.c_int32), ("decode_ids", _p), ("decode_context_lens", _p),
+                ("decode_block_table", _p), ("decode_max_context", ctypes.c_int32),
+                ("n_prefill", ctypes.c_int32), ("prefill_ids", _p), ("prefill_prefix_lens", _p),
+                ("prefill_cu_chunk_lens", _p), ("prefill_block_table", _p),
+                ("prefill_total_tokens", ctypes.c_int32), ("prefill_max_chunk", ctypes.c_int32),
+                ("prefill_max_context", ctypes.c_int32),
+                ("n_first", ctypes.c_int32), ("first_token_ids", _p),
+                ("n_finished", ctypes.c_int32), ("finished_ids", _p)]
 
 
 def _hip_runtimes_mapped() -> set[str]:
@@ -92,6 +107,11 @@ def _load() -> ctypes.CDLL:
         "kvc_prefix_cache_release": (c_i32, [vp, vp, c_i32]),
         "kvc_prefix_cache_refcount": (c_i32, [vp, c_i32]),
         "kvc_prefix_cache_counts": (c_i32, [vp, vp, vp, vp]),
+        "kvc_sched_create": (vp, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+        "kvc_sched_destroy": (None, [vp]),
+        "kvc_sched_submit": (c_i32, [vp, c_i32, c_i32]),
+        "kvc_sched_unfinished": (c_i32, [vp]),
+        "kvc_sched_next_step": (c_i32, [vp, ctypes.POINTER(_CStep)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -387,3 +407,75 @@ class PrefixCache:
         _check("kvc_prefix_cache_counts", LIB.kvc_prefix_cache_counts(
             self._h, ctypes.byref(f), ctypes.byref(c), ctypes.byref(r)))
         return f.value, c.value, r.value
+
+
+SCHED_PREFILL_FIRST = 0
+SCHED_DECODE_FIRST = 1
+SCHED_STATIC = 2
+
+
+@dataclasses.dataclass
+class SchedStep:
+    """One step built by :class:`Scheduler` (host int32 arrays)."""
+    decode_ids: np.ndarray
+    decode_context_lens: np.ndarray
+    decode_block_table: np.ndarray     # [n_decode, max_blocks], unused columns -1
+    decode_max_context: int
+    prefill_ids: np.ndarray
+    prefill_prefix_lens: np.ndarray
+    prefill_cu_chunk_lens: np.ndarray  # [n_prefill + 1]
+    prefill_block_table: np.ndarray    # [n_prefill, max_blocks]
+    prefill_total_tokens: int
+    prefill_max_chunk: int
+    prefill_max_context: int
+    first_token_ids: np.ndarray
+    finished_ids: np.ndarray
+
+
+class Scheduler:
+    """Iteration-level scheduler and step builder (include/kvc_sched.h)."""
+
+    def __init__(self, policy: int, slots: int, token_budget: int, num_blocks: int,
+                 max_blocks_per_seq: int):
+        self._h = LIB.kvc_sched_create(int(policy), int(slots), int(token_budget),
+                                       int(num_blocks), int(max_blocks_per_seq))
+        if not self._h:
+            raise KvcError("kvc_sched_create", -2, "bad policy or sizes, or out of memory")
+        self.slots, self.max_blocks = int(slots), int(max_blocks_per_seq)
+        n, m = self.slots, self.max_blocks
+        self._buf = {k: np.zeros(sz, np.int32) for k, sz in (
+            ("decode_ids", n), ("decode_context_lens", n), ("decode_block_table", n * m),
+            ("prefill_ids", n), ("prefill_prefix_lens", n), ("prefill_cu_chunk_lens", n + 1),
+            ("prefill_block_table", n * m), ("first_token_ids", n), ("finished_ids", n))}
+        self._c = _CStep(**{k: v.ctypes.data_as(_CStep._p) for k, v in self._buf.items()})
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            LIB.kvc_sched_destroy(h)
+
+    def submit(self, prompt_len: int, answer_len: int) -> int:
+        r = LIB.kvc_sched_submit(self._h, int(prompt_len), int(answer_len))
+        _check("kvc_sched_submit", min(r, 0))
+        return r
+
+    def unfinished(self) -> int:
+        return LIB.kvc_sched_unfinished(self._h)
+
+    def next_step(self) -> SchedStep | None:
+        """The next step, or None when nothing is queued or running. Raises
+        KvcError (status KVC_ERR_NO_BLOCKS) when the pool cannot cover it."""
+        r = LIB.kvc_sched_next_step(self._h, ctypes.byref(self._c))
+        _check("kvc_sched_next_step", min(r, 0))
+        if r == 0:
+            return None
+        c, b, m = self._c, self._buf, self.max_blocks
+        nd, npf = c.n_decode, c.n_prefill
+        return SchedStep(
+            b["decode_ids"][:nd].copy(), b["decode_context_lens"][:nd].copy(),
+            b["decode_block_table"][:nd * m].reshape(nd, m).copy(), c.decode_max_context,
+            b["prefill_ids"][:npf].copy(), b["prefill_prefix_lens"][:npf].copy(),
+            b["prefill_cu_chunk_lens"][:npf + 1].copy(),
+            b["prefill_block_table"][:npf * m].reshape(npf, m).copy(),
+            c.prefill_total_tokens, c.prefill_max_chunk, c.prefill_max_context,
+            b["first_token_ids"][:c.n_first].copy(), b["finished_ids"][:c.n_finished].copy())

@@ -22,6 +22,7 @@ extern "C" const char* kvc_status_string(int status) {
     case KVC_ERR_LAUNCH: return "kernel launch failed";
     case KVC_ERR_NO_BLOCKS: return "not enough free or reusable blocks";
     case KVC_ERR_STATE: return "block not held, out of range, or cached under another prefix";
+    case KVC_ERR_NO_MEMORY: return "host memory ran out";
   }
   return "unknown status";
 }

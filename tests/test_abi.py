@@ -127,6 +127,6 @@ def test_zero_sized_calls_launch_nothing():
 
 
 def test_status_strings():
-    for s in range(-8, 1):
+    for s in range(-9, 1):
         assert LIB.kvc_status_string(s)
     assert LIB.kvc_status_string(-99) == b"unknown status"
