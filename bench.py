@@ -47,7 +47,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--workload", default="c3-decode",
-                    choices=["c3-decode", "c4-mixed", "c5-decode", "c5-prefill", "prefix-warm"])
+                    choices=["c3-decode", "c4-mixed", "c5-decode", "c5-prefill", "prefix-warm",
+                             "queue-replay"])
+    ap.add_argument("--direct-steps", type=int, default=400,
+                    help="queue-replay: leading steps of each continuous plan run for real")
     return ap.parse_args()
 
 
@@ -148,6 +151,8 @@ def main():
         return bench_prefix_warm(args)
     if args.workload == "c4-mixed":
         return bench_c4_mixed(args)
+    if args.workload == "queue-replay":
+        return bench_queue_replay(args)
 
     import torch
 
@@ -553,6 +558,165 @@ def bench_prefix_warm(args):
     res["cold_tflops"] = round(pairs_cold * 4 * D * L / (ms_cold * 1e-3) / 1e12, 1)
     res["speedup_cold_over_warm"] = round(ms_cold / ms_warm, 2)
     res["host_match_us"] = round(match_us, 1)
+    print(json.dumps(res), flush=True)
+
+
+# the aiwithghost page's simulated queue table (Node on one CPU thread, a tiny
+# random-weight model): context for the shape of the results, not a target
+PAGE_QUEUE_TABLE = {
+    "one at a time, no cache": (452.2, 851.5, 892.3, 64),
+    "one at a time, KV cache": (23.9, 45.1, 47.3, 1203),
+    "static batches of 16, cache": (21.2, 40.5, 42.8, 1331),
+    "continuous batching, 16 slots": (13.8, 26.4, 27.8, 2044),
+}
+
+
+def bench_queue_replay(args):
+    """The lab's queue replay on MI355X: 1,000 requests at t = 0 (prompts 8-32,
+    answers 16-96 tokens), 16 slots. Step times of the attention path (32
+    layers of GQA 32/8/128 bf16 attention: the fused append + decode launch for
+    decode rows, the chunked-prefill launch for prompts) are measured over a
+    grid of batch rows x lengths, each grid point one HIP graph of the 32
+    layers' launches replayed between two events; the native scheduler plans
+    every policy and the replay sums interpolated shares, as the lab does.
+    Then the leading steps of each continuous plan are run for real (each step
+    captured as a graph of its own descriptors) and their measured time is set
+    against the estimate for the same steps."""
+    import torch
+
+    import kv_cache_decode_append_amd as kvc
+    import workloads as W
+    from kv_cache_decode_append_amd import replay as R
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.P1
+    Hq, Hkv, D, L = w.Hq, w.Hkv, w.D, w.layers
+    slots = W.QUEUE_SLOTS
+    prompts, answers = W.queue_requests()
+    max_blocks = W.blocks_for(max(p + a - 1 for p, a in zip(prompts, answers)))
+    nb = slots * max_blocks
+    caches = [kvc.PagedKVCache.allocate(nb, Hkv, D, torch.bfloat16, device=dev) for _ in range(L)]
+    for c in caches:
+        c.k_cache.normal_(0, 0.5)
+        c.v_cache.normal_(0, 0.5)
+    max_rows = slots * 128
+    q = torch.empty(max_rows, Hq, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
+    kv = torch.empty(max_rows, Hkv, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
+    out = torch.empty_like(q)
+    scale = 1.0 / D ** 0.5
+    reps = max(5, args.steps // 5)
+
+    def graph_ms(launch, reps):
+        launch()                      # eager once (also checks the arguments)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            launch()
+        g.replay()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    def decode_launch(n, bt, ctx, max_ctx):
+        def run():
+            for c in caches:
+                kvc.decode_append_attention(c, q[:n], kv[:n], kv[:n], bt, ctx, max_ctx, scale,
+                                            out=out[:n])
+        return run
+
+    def prefill_launch(total, cu, pre, bt, max_chunk):
+        def run():
+            for c in caches:
+                kvc.chunked_prefill_attention(c, q[:total], kv[:total], kv[:total], cu, pre, bt,
+                                              max_chunk, scale, out=out[:total])
+        return run
+
+    # 1. the grid
+    rows = [1, 2, 4, 8, 16]
+    lengths = [8, 16, 24, 32, 48, 64, 96, 128]
+    grid_bt = torch.arange(nb, dtype=torch.int32, device=dev).reshape(slots, max_blocks)
+    dec_ms = [[0.0] * len(lengths) for _ in rows]
+    pf_ms = [[0.0] * len(lengths) for _ in rows]
+    t0 = time.perf_counter()
+    for i, n in enumerate(rows):
+        for j, ln in enumerate(lengths):
+            ctx = torch.full((n,), ln, dtype=torch.int32, device=dev)
+            dec_ms[i][j] = graph_ms(decode_launch(n, grid_bt[:n], ctx, ln), reps)
+            cu = torch.arange(0, (n + 1) * ln, ln, dtype=torch.int32, device=dev)
+            pre = torch.zeros(n, dtype=torch.int32, device=dev)
+            pf_ms[i][j] = graph_ms(prefill_launch(n * ln, cu, pre, grid_bt[:n], ln), reps)
+        print(f"[queue-replay] grid rows={n} done ({time.perf_counter() - t0:.1f} s)",
+              file=sys.stderr, flush=True)
+    times = R.StepTimes(rows, lengths, dec_ms, pf_ms)
+
+    # 2. plans and the replay estimate
+    answer_tokens = int(sum(answers))
+    table, plans = {}, {}
+    for pol in R.queue_policies(slots):
+        steps = R.plan(pol, prompts, answers)
+        costs = [R.step_cost_ms(st, times, pol.recompute) for st in steps]
+        res = R.replay(steps, costs, len(prompts))
+        summ = R.summarize(res, answer_tokens)
+        summ = {k: round(v, 4) for k, v in summ.items()}
+        summ["steps"] = len(steps)
+        table[pol.name] = summ
+        plans[pol.name] = (steps, costs)
+    print(f"[queue-replay] replay done ({time.perf_counter() - t0:.1f} s)", file=sys.stderr,
+          flush=True)
+
+    # 3. the leading steps of the continuous plans, run for real
+    direct = {}
+    for name in (f"continuous batching, {slots} slots",
+                 f"continuous batching, {slots} slots, decode first"):
+        steps, costs = plans[name]
+        k = min(args.direct_steps, len(steps))
+        real = 0.0
+        for st in steps[:k]:
+            parts = []
+            if len(st.decode_ids):
+                n = len(st.decode_ids)
+                bt = torch.from_numpy(st.decode_block_table).to(dev)
+                ctx = torch.from_numpy(st.decode_context_lens).to(dev)
+                parts.append(decode_launch(n, bt, ctx, st.decode_max_context))
+            if len(st.prefill_ids):
+                bt = torch.from_numpy(st.prefill_block_table).to(dev)
+                cu = torch.from_numpy(st.prefill_cu_chunk_lens).to(dev)
+                pre = torch.from_numpy(st.prefill_prefix_lens).to(dev)
+                parts.append(prefill_launch(st.prefill_total_tokens, cu, pre, bt,
+                                            st.prefill_max_chunk))
+            real += graph_ms(lambda: [f() for f in parts], 3)
+        est = float(sum(costs[:k]))
+        direct[name] = {"steps": k, "measured_ms": round(real, 3), "estimated_ms": round(est, 3),
+                        "measured_over_estimated": round(real / est, 4)}
+        print(f"[queue-replay] direct {name}: {k} steps ({time.perf_counter() - t0:.1f} s)",
+              file=sys.stderr, flush=True)
+
+    head = table[f"continuous batching, {slots} slots"]
+    res = _base_line(args, "queue replay answer tokens/s, continuous batching with 16 slots, "
+                     "1,000 requests at t = 0 (attention path, 32 layers, measured step times)",
+                     round(head["tokens_per_s"], 1), "tokens/s",
+                     head["all_done_s"] * 1e3 / head["steps"], "bf16",
+                     {"workload": "1,000 requests at t = 0, prompts 8-32 tokens, answers 16-96 "
+                                  "tokens (uniform), 16 slots, GQA 32/8, head_dim 128, bf16, "
+                                  "32 layers of attention per step",
+                      "requests": len(prompts), "answer_tokens": answer_tokens, "slots": slots,
+                      "prefill_token_budget": 2048, "layers": L},
+                     None)
+    res["steps"] = head["steps"]
+    res["warmup"] = 1
+    res["queue_table"] = table
+    res["page_queue_table"] = {k: dict(zip(("median_ttft_s", "p95_ttft_s", "all_done_s",
+                                            "tokens_per_s"), v))
+                               for k, v in PAGE_QUEUE_TABLE.items()}
+    res["step_time_grid_ms"] = {"rows": rows, "lengths": lengths, "decode": dec_ms,
+                                "prefill": pf_ms}
+    res["direct_check"] = direct
     print(json.dumps(res), flush=True)
 
 

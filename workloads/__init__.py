@@ -201,3 +201,21 @@ def prefix_values(w: Workload, tokens) -> tuple[np.ndarray, np.ndarray, np.ndarr
         v[p] = rng.standard_normal((w.Hkv, w.D), dtype=np.float32) * w.sigma
         q[p] = rng.standard_normal((w.Hq, w.D), dtype=np.float32) * w.sigma
     return k, v, q
+
+
+# ---- request queue (aiwithghost page, section "What our lab measured") -------
+
+QUEUE_SEED = 777777
+QUEUE_N = 1000
+QUEUE_SLOTS = 16
+QUEUE_PROMPT = (8, 32)     # inclusive ranges
+QUEUE_ANSWER = (16, 96)
+
+
+def queue_requests(n: int = QUEUE_N, seed: int = QUEUE_SEED):
+    """Prompt and answer lengths of ``n`` requests, all arriving at t = 0, drawn
+    uniformly from the inclusive ranges the lab's simulated queue states."""
+    rng = np.random.default_rng(seed)
+    prompts = rng.integers(QUEUE_PROMPT[0], QUEUE_PROMPT[1] + 1, n)
+    answers = rng.integers(QUEUE_ANSWER[0], QUEUE_ANSWER[1] + 1, n)
+    return prompts.astype(np.int64).tolist(), answers.astype(np.int64).tolist()
