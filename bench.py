@@ -57,6 +57,7 @@ def parse():
 # Files the decode kernel is compiled from; the traffic figure is only valid
 # for the exact sources the counters were taken on.
 DECODE_SOURCES = ("kv_cache_decode_append_amd/csrc/kvc_decode.hip",
+                  "kv_cache_decode_append_amd/csrc/kvc_decode_item.h",
                   "kv_cache_decode_append_amd/csrc/kvc_device.h",
                   "kv_cache_decode_append_amd/csrc/kvc_host.h",
                   "include/kvc.h")
@@ -386,8 +387,9 @@ def bench_c4_mixed(args):
     lengths (median 6,000, tail clipped at 32,000); 206 decode one token each
     (one fused append + attention launch, split over partitions for the long
     ones) and 4 run a 2,048-token prefill chunk over their prefix (one launch).
-    One layer's pool (~6.5 GB, far larger than the caches) is timed per step
-    and reported per layer and for 32 layers."""
+    The same step is also timed as ONE launch of the mixed-batch kernel. One
+    layer's pool (~6.5 GB, far larger than the caches) is timed per step and
+    reported per layer and for 32 layers."""
     import torch
 
     import kv_cache_decode_append_amd as kvc
@@ -436,10 +438,38 @@ def bench_c4_mixed(args):
         dec(i)
         pre(i)
 
+    mws = torch.zeros(kvc.mixed_workspace_bytes(nd, max_dec, Hq, Hkv, D), dtype=torch.uint8,
+                      device=dev)
+
+    def one_launch(i):
+        kvc.mixed_step_attention(
+            cache, Hq, q_decode=q_dec, k_new=k_dec, v_new=v_dec, decode_block_table=bt_dec,
+            decode_context_lens=ctx_dec, decode_max_context=max_dec, q_prefill=q_pre,
+            k_prefill=k_pre, v_prefill=v_pre, cu_chunk_lens=cu, prefix_lens=prefix,
+            prefill_block_table=bt_pre, prefill_max_chunk=chunk, out_decode=out_dec,
+            out_prefill=out_pre, workspace=mws)
+
     ms_dec = _timed(dec, args.steps, args.warmup)
     ms_pre = _timed(pre, max(1, args.steps // 4), max(1, args.warmup // 4))
     ms_step = _timed(step, max(1, args.steps // 4), max(1, args.warmup // 4))
+    ms_one = _timed(one_launch, max(1, args.steps // 4), max(1, args.warmup // 4))
+
+    def one_launch_dec(i):
+        kvc.mixed_step_attention(
+            cache, Hq, q_decode=q_dec, k_new=k_dec, v_new=v_dec, decode_block_table=bt_dec,
+            decode_context_lens=ctx_dec, decode_max_context=max_dec, out_decode=out_dec,
+            workspace=mws)
+
+    def one_launch_pre(i):
+        kvc.mixed_step_attention(
+            cache, Hq, q_prefill=q_pre, k_prefill=k_pre, v_prefill=v_pre, cu_chunk_lens=cu,
+            prefix_lens=prefix, prefill_block_table=bt_pre, prefill_max_chunk=chunk,
+            out_prefill=out_pre, workspace=mws)
+
+    ms_one_dec = _timed(one_launch_dec, max(1, args.steps // 4), max(1, args.warmup // 4))
+    ms_one_pre = _timed(one_launch_pre, max(1, args.steps // 4), max(1, args.warmup // 4))
     assert int(cache.err_flag.item()) == 0
+    assert int(mws[:256].count_nonzero().item()) == 0
     kv_dec = int(ctx[dec_rows].sum()) * Hkv * D * 2 * 2
     pairs = sum(Hq * (chunk * (int(c) - chunk) + chunk * (chunk + 1) // 2) for c in ctx[pre_rows])
     flop = pairs * 4 * D
@@ -460,6 +490,11 @@ def bench_c4_mixed(args):
     res["prefill_ms_per_layer"] = round(ms_pre, 4)
     res["step_ms_per_layer"] = round(ms_step, 4)
     res["step_ms_32_layers"] = round(ms_step * L, 3)
+    res["one_launch_step_ms_per_layer"] = round(ms_one, 4)
+    res["one_launch_step_ms_32_layers"] = round(ms_one * L, 3)
+    res["one_launch_speedup"] = round(ms_step / ms_one, 3)
+    res["one_launch_decode_only_ms"] = round(ms_one_dec, 4)
+    res["one_launch_prefill_only_ms"] = round(ms_one_pre, 4)
     res["prefill_tflops"] = round(tf, 1)
     res["prefill_mfma_frac"] = round(tf / 2500.0, 4)
     print(json.dumps(res), flush=True)

@@ -73,7 +73,9 @@ enum {
 enum {
   KVC_DEVERR_BLOCK_ID = 1,  /* block table entry outside [0, num_blocks) */
   KVC_DEVERR_SLOT = 2,      /* slot outside [0, num_blocks * block_size) */
-  KVC_DEVERR_CONTEXT = 4    /* context needs more blocks than the table row has */
+  KVC_DEVERR_CONTEXT = 4,   /* context needs more blocks than the table row has */
+  KVC_DEVERR_QUEUE = 8      /* mixed-batch kernel: a wait for its first phase gave up (the
+                               workspace header was not zero at the start of the call) */
 };
 
 /* One layer's paged cache. Pointers are device memory owned by the caller. */
@@ -210,6 +212,67 @@ int kvc_chunked_prefill_attention_split(const kvc_cache* cache, const void* q, c
                                         int32_t max_blocks, int32_t Hq, float softmax_scale,
                                         void* out, void* workspace, size_t workspace_bytes,
                                         void* stream);
+
+/* One continuous-batching step in ONE launch: decode rows and prefill chunks
+ * together (aiwithghost.com "KV cache and continuous batching: 1,000 people
+ * ask AI", section "How does continuous batching share the server?": the batch
+ * is rebuilt every step and newly admitted requests start with their prefill
+ * next to rows that decode; gouthm.com "The KV cache is not your bottleneck",
+ * section "The fix that mattered": decode rows plus prefill chunks under a
+ * token budget). Computes what kvc_decode_append_attention (decode rows) and
+ * kvc_chunked_prefill_attention (chunks) compute, in a persistent kernel whose
+ * workgroups take work items from a device queue: first the new K/V writes
+ * and a longest-first order of the decode rows, then prefill query tiles and
+ * whole decode rows (per kv head) interleaved, each kind largest first.
+ * Prefill rows equal kvc_chunked_prefill_attention's bit for bit; decode rows
+ * are the same computation with a row's blocks spread over 8 waves of one
+ * workgroup instead of split over workgroups (another summation order).
+ * Fields: the arguments of those two calls; a part with count 0 may leave its
+ * pointers NULL. Decode rows and prefill chunks must belong to different
+ * sequences (their blocks may alias only where both only read, e.g. a shared
+ * cached prefix). */
+typedef struct {
+  int32_t n_decode;                   /* decode rows, <= 4096 */
+  const void* q_decode;               /* [n_decode][Hq][head_dim] */
+  const void* k_new;                  /* [n_decode][num_kv_heads][head_dim], position ctx - 1 */
+  const void* v_new;
+  const int32_t* decode_block_table;  /* [n_decode][decode_max_blocks] */
+  int32_t decode_max_blocks;
+  const int32_t* decode_context_lens; /* [n_decode], counting the new token */
+  int32_t decode_max_context;         /* host-known bound of decode_context_lens */
+  void* out_decode;                   /* [n_decode][Hq][head_dim] */
+  int32_t n_prefill;                  /* prefill chunks */
+  const void* q_prefill;              /* [prefill_total_tokens][Hq][head_dim] */
+  const void* k_prefill;              /* [prefill_total_tokens][num_kv_heads][head_dim] */
+  const void* v_prefill;
+  const int32_t* cu_chunk_lens;       /* [n_prefill + 1] */
+  const int32_t* prefix_lens;         /* [n_prefill] */
+  int32_t prefill_total_tokens;
+  int32_t prefill_max_chunk;
+  const int32_t* prefill_block_table; /* [n_prefill][prefill_max_blocks] */
+  int32_t prefill_max_blocks;
+  void* out_prefill;                  /* [prefill_total_tokens][Hq][head_dim] */
+} kvc_mixed_batch;
+
+/* Bytes of workspace kvc_mixed_step_attention needs: a 256-byte queue header
+ * and the decode row order (256 + n_decode * 4, rounded up to 256). 0 for
+ * invalid sizes. */
+size_t kvc_mixed_workspace_bytes(int32_t n_decode, int32_t decode_max_context, int32_t Hq,
+                                 int32_t num_kv_heads, int32_t head_dim);
+
+/* Runs one mixed step (see kvc_mixed_batch) on `stream`.
+ *   workspace  device memory of >= kvc_mixed_workspace_bytes(...) bytes, 16-byte
+ *              aligned. Its first 256 bytes (the queue header) must be zero
+ *              when a call starts: zero them once when the workspace is
+ *              allocated; every call leaves them zero again. Calls that share
+ *              a workspace must not overlap (same stream, or ordered).
+ * Supported: bf16 caches with head_dim 64 or 128 and fp32 caches with head_dim
+ * 32, G = Hq / num_kv_heads in {1, 2, 4}; KVC_ERR_UNSUPPORTED otherwise.
+ * Returns KVC_ERR_WORKSPACE for a missing or short workspace and validates
+ * like the two calls it replaces. */
+int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_batch* batch, int32_t Hq,
+                             float softmax_scale, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Static string for a status code. */
 const char* kvc_status_string(int status);

@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     BLOCK_SIZE,
     DEVERR_BLOCK_ID,
     DEVERR_CONTEXT,
+    DEVERR_QUEUE,
     DEVERR_SLOT,
     KVC_BF16,
     KVC_F32,
@@ -27,6 +28,8 @@ from ._lib import (  # noqa: F401
     decode_workspace_bytes,
     kv_append,
     kv_bytes_per_token,
+    mixed_step_attention,
+    mixed_workspace_bytes,
     paged_decode_attention,
     prefill_workspace_bytes,
     slot_mapping,

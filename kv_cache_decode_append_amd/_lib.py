@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvc.so")
 
 KVC_F32, KVC_BF16 = 0, 1
-DEVERR_BLOCK_ID, DEVERR_SLOT, DEVERR_CONTEXT = 1, 2, 4
+DEVERR_BLOCK_ID, DEVERR_SLOT, DEVERR_CONTEXT, DEVERR_QUEUE = 1, 2, 4, 8
 BLOCK_SIZE = 16
 
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
@@ -55,6 +55,21 @@ class _CStep(ctypes.Structure):
                 ("prefill_max_context", ctypes.c_int32),
                 ("n_first", ctypes.c_int32), ("first_token_ids", _p),
                 ("n_finished", ctypes.c_int32), ("finished_ids", _p)]
+
+
+class _CMixed(ctypes.Structure):
+    """kvc_mixed_batch (include/kvc.h)."""
+    _fields_ = [("n_decode", ctypes.c_int32), ("q_decode", ctypes.c_void_p),
+                ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+                ("decode_block_table", ctypes.c_void_p), ("decode_max_blocks", ctypes.c_int32),
+                ("decode_context_lens", ctypes.c_void_p), ("decode_max_context", ctypes.c_int32),
+                ("out_decode", ctypes.c_void_p),
+                ("n_prefill", ctypes.c_int32), ("q_prefill", ctypes.c_void_p),
+                ("k_prefill", ctypes.c_void_p), ("v_prefill", ctypes.c_void_p),
+                ("cu_chunk_lens", ctypes.c_void_p), ("prefix_lens", ctypes.c_void_p),
+                ("prefill_total_tokens", ctypes.c_int32), ("prefill_max_chunk", ctypes.c_int32),
+                ("prefill_block_table", ctypes.c_void_p), ("prefill_max_blocks", ctypes.c_int32),
+                ("out_prefill", ctypes.c_void_p)]
 
 
 def _hip_runtimes_mapped() -> set[str]:
@@ -107,6 +122,8 @@ def _load() -> ctypes.CDLL:
         "kvc_prefix_cache_release": (c_i32, [vp, vp, c_i32]),
         "kvc_prefix_cache_refcount": (c_i32, [vp, c_i32]),
         "kvc_prefix_cache_counts": (c_i32, [vp, vp, vp, vp]),
+        "kvc_mixed_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+        "kvc_mixed_step_attention": (c_int, [P, ctypes.POINTER(_CMixed), c_i32, fl, vp, c_sz, vp]),
         "kvc_sched_create": (vp, [c_i32, c_i32, c_i32, c_i32, c_i32]),
         "kvc_sched_destroy": (None, [vp]),
         "kvc_sched_submit": (c_i32, [vp, c_i32, c_i32]),
@@ -342,6 +359,95 @@ def chunked_prefill_attention(cache: PagedKVCache, q: torch.Tensor, k: torch.Ten
         block_table.data_ptr(), block_table.shape[1], Hq, scale, out.data_ptr(),
         _ptr(workspace), ws_bytes, _stream()))
     return out
+
+
+def mixed_workspace_bytes(n_decode: int, decode_max_context: int, Hq: int, num_kv_heads: int,
+                          head_dim: int) -> int:
+    return int(LIB.kvc_mixed_workspace_bytes(n_decode, decode_max_context, Hq, num_kv_heads,
+                                             head_dim))
+
+
+def mixed_step_attention(cache: PagedKVCache, Hq: int, *, q_decode=None, k_new=None, v_new=None,
+                         decode_block_table=None, decode_context_lens=None,
+                         decode_max_context: int = 0, q_prefill=None, k_prefill=None,
+                         v_prefill=None, cu_chunk_lens=None, prefix_lens=None,
+                         prefill_block_table=None, prefill_max_chunk: int = 0,
+                         softmax_scale: float | None = None, out_decode=None, out_prefill=None,
+                         workspace: torch.Tensor | None = None):
+    """One mixed continuous-batching step in one launch (kvc_mixed_step_attention):
+    decode rows as decode_append_attention takes them, prefill chunks as
+    chunked_prefill_attention takes them. Returns (out_decode, out_prefill),
+    either None when its part is empty. ``workspace`` must have its first 256
+    bytes zero before the first call (each call leaves them zero); one of the
+    size the library asks for is made with torch.zeros when none is given."""
+    dev = cache.k_cache.device
+    D = cache.head_dim
+    b = _CMixed()
+    if q_decode is not None and q_decode.shape[0] > 0:
+        _need(q_decode, "q_decode", cache.dtype, 3, dev)
+        n = q_decode.shape[0]
+        if q_decode.shape != (n, Hq, D):
+            raise ValueError(f"q_decode must be [{n}, {Hq}, {D}]")
+        for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+            _need(t, nm, cache.dtype, 3, dev)
+            if t.shape != (n, cache.num_kv_heads, D):
+                raise ValueError(f"{nm} must be [{n}, {cache.num_kv_heads}, {D}]")
+        _need(decode_block_table, "decode_block_table", torch.int32, 2, dev)
+        _need(decode_context_lens, "decode_context_lens", torch.int32, 1, dev)
+        if decode_block_table.shape[0] != n or decode_context_lens.shape[0] != n:
+            raise ValueError("decode block table / context lengths disagree with q_decode")
+        if out_decode is None:
+            out_decode = torch.empty_like(q_decode)
+        _need(out_decode, "out_decode", cache.dtype, 3, dev)
+        if out_decode.shape != q_decode.shape:
+            raise ValueError("out_decode must have q_decode's shape")
+        b.n_decode, b.q_decode, b.k_new, b.v_new = n, q_decode.data_ptr(), k_new.data_ptr(), \
+            v_new.data_ptr()
+        b.decode_block_table, b.decode_max_blocks = decode_block_table.data_ptr(), \
+            decode_block_table.shape[1]
+        b.decode_context_lens, b.decode_max_context = decode_context_lens.data_ptr(), \
+            int(decode_max_context)
+        b.out_decode = out_decode.data_ptr()
+    else:
+        out_decode = None
+    if q_prefill is not None and q_prefill.shape[0] > 0:
+        _need(q_prefill, "q_prefill", cache.dtype, 3, dev)
+        total = q_prefill.shape[0]
+        if q_prefill.shape != (total, Hq, D):
+            raise ValueError(f"q_prefill must be [{total}, {Hq}, {D}]")
+        for t, nm in ((k_prefill, "k_prefill"), (v_prefill, "v_prefill")):
+            _need(t, nm, cache.dtype, 3, dev)
+            if t.shape != (total, cache.num_kv_heads, D):
+                raise ValueError(f"{nm} must be [{total}, {cache.num_kv_heads}, {D}]")
+        _need(cu_chunk_lens, "cu_chunk_lens", torch.int32, 1, dev)
+        _need(prefix_lens, "prefix_lens", torch.int32, 1, dev)
+        _need(prefill_block_table, "prefill_block_table", torch.int32, 2, dev)
+        m = prefix_lens.shape[0]
+        if cu_chunk_lens.shape[0] != m + 1 or prefill_block_table.shape[0] != m:
+            raise ValueError("cu_chunk_lens / prefix_lens / prefill_block_table disagree")
+        if out_prefill is None:
+            out_prefill = torch.empty_like(q_prefill)
+        _need(out_prefill, "out_prefill", cache.dtype, 3, dev)
+        if out_prefill.shape != q_prefill.shape:
+            raise ValueError("out_prefill must have q_prefill's shape")
+        b.n_prefill, b.q_prefill = m, q_prefill.data_ptr()
+        b.k_prefill, b.v_prefill = k_prefill.data_ptr(), v_prefill.data_ptr()
+        b.cu_chunk_lens, b.prefix_lens = cu_chunk_lens.data_ptr(), prefix_lens.data_ptr()
+        b.prefill_total_tokens, b.prefill_max_chunk = total, int(prefill_max_chunk)
+        b.prefill_block_table, b.prefill_max_blocks = prefill_block_table.data_ptr(), \
+            prefill_block_table.shape[1]
+        b.out_prefill = out_prefill.data_ptr()
+    else:
+        out_prefill = None
+    need = mixed_workspace_bytes(b.n_decode, b.decode_max_context, Hq, cache.num_kv_heads, D)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", device=dev)
+    scale = (1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
+    _check("kvc_mixed_step_attention", LIB.kvc_mixed_step_attention(
+        cache.c, ctypes.byref(b), int(Hq), scale, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return out_decode, out_prefill
 
 
 KVC_ERR_NO_BLOCKS = -7

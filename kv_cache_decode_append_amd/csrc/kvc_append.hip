@@ -90,22 +90,9 @@ __global__ void chunk_append_kernel(uint8_t* __restrict__ kc, uint8_t* __restric
   const int32_t c = (int32_t)(i - row * nc);
   const int32_t r = (int32_t)(row / hkv);
   const int32_t h = (int32_t)(row - (int64_t)r * hkv);
-  const int32_t p = p0 + r;
-  const int32_t lb = p >> 4;
-  if (lb >= max_blocks) {
-    if (h == 0 && c == 0) flag_error(err, KVC_DEVERR_CONTEXT);
-    return;
-  }
-  const int32_t blk = block_table[(int64_t)s * max_blocks + lb];
-  if (blk < 0 || blk >= num_blocks) {
-    if (h == 0 && c == 0) flag_error(err, KVC_DEVERR_BLOCK_ID);
-    return;
-  }
-  const int64_t row_bytes = (int64_t)nc * 16;
-  const int64_t dst = (((int64_t)blk * hkv + h) * 16 + (p & 15)) * row_bytes + (int64_t)c * 16;
-  const int64_t src = (((int64_t)(t0 + r) * hkv + h) * nc + c) * 16;
-  *reinterpret_cast<u32x4*>(kc + dst) = *reinterpret_cast<const u32x4*>(k + src);
-  *reinterpret_cast<u32x4*>(vc + dst) = *reinterpret_cast<const u32x4*>(v + src);
+  const int bad = chunk_append_one(kc, vc, k, v, block_table + (int64_t)s * max_blocks, max_blocks,
+                                   num_blocks, hkv, nc, t0, p0, r, h, c);
+  if (bad && h == 0 && c == 0) flag_error(err, bad);
 }
 
 int launch_chunk_append(const kvc_cache* c, const void* k, const void* v, int32_t n_seqs,

@@ -1,0 +1,492 @@
+// Internal: the paged GQA decode work item, shared by the decode kernel and
+// the mixed-batch kernel.
+//
+// Each decode step attends the new query over every key and value stored for its
+// sequence (aiwithghost.com "KV cache and continuous batching: 1,000 people ask
+// AI", section "What does a KV cache keep?"; daviddominguez.dev "The KV cache
+// and prefix caching", section "What prefill stores and decode reads"), reading
+// them through the sequence's block table (same page, PagedAttention design),
+// with several query heads sharing one K/V head (same page, grouped-query
+// attention). The read of the whole cache is what grows with context (same page,
+// section "The prompt is paid once, the output is paid every step"), so this
+// kernel is HBM-bound: it is built to stream K/V at full bandwidth.
+//
+// Work decomposition (one work item = NW waves: 4 in the decode kernel, 8 in
+// the mixed-batch kernel):
+//   item = (partition, kv_head, sequence). A partition is `part_blocks`
+//   consecutive 16-token blocks of one sequence. Wave w of the item walks
+//   blocks w, w+NW, w+2NW, ... of the partition on its own (no barriers in the
+//   main loop), keeping an online-softmax state (m, l, acc) for the G query heads of
+//   its kv head, so every K/V tile is read from HBM exactly once per kv head.
+//   At the end the NW wave states are merged in LDS; a sequence that spans
+//   several partitions writes (m, l, acc) partials that decode_merge_kernel
+//   combines with the log-sum-exp rule.
+//
+// Per block (one contiguous (block, kv-head) tile of 16 x head_dim for K and for V):
+//   * K and V tiles arrive through 16-byte non-temporal buffer loads (each tile
+//     is read once per step), in a register ring of 2-3 blocks per wave. A
+//     buffer descriptor of zero bytes turns the prefetch past the wave's last
+//     block into a no-op with no memory traffic.
+//   * QK: K goes to a per-wave LDS tile with an XOR swizzle of its 16-byte
+//     chunks (conflict-free row reads); lane (h, t) computes the full dot product
+//     of query head h with token t's key (bf16: v_dot2_f32_bf16, fp32: FMA), so
+//     no cross-lane sum is needed. Scores are in the log2 domain (scale*log2 e).
+//   * softmax: max and sum over the 16 tokens of a head are DPP reductions
+//     inside a row of 16 lanes (8 lanes x 2 for G = 8).
+//   * PV: lane owns one 16-byte chunk of a V row and accumulates all G heads;
+//     the accumulator is rescaled only when some head's running max moved.
+
+#pragma once
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "kvc.h"
+#include "kvc_device.h"
+
+namespace kvc {
+
+constexpr int kMinPartBlocks = 16;
+
+template <typename T, int D, int G, int NW>
+struct DecodeShape {
+  static constexpr int MAX_PART = NW * 64;     // blocks per partition: one block id per lane
+  static constexpr int EB = ElemBytes<T>::value;
+  static constexpr int RB = D * EB;             // bytes of one token row of one head
+  static constexpr int NC = RB / 16;            // 16-byte chunks per row
+  static constexpr int CE = 16 / EB;            // elements per chunk
+  static constexpr int TILE = 16 * RB;          // one (block, kv head) tile, bytes
+  static constexpr int QS = 2;                  // lanes sharing one (head, token) dot product
+  static constexpr int NCQ = NC / QS;           // query chunks held per lane
+  static constexpr int LPH = (G == 8) ? 8 : 16; // QK lanes per query head (one DPP row or half)
+  static constexpr int TPS = LPH / QS;          // tokens per QK sub-step
+  static constexpr int SPL = 16 / TPS;          // QK sub-steps per block
+  static constexpr int TPI = 64 / NC;           // V tokens covered by one wave load
+  static constexpr int NI = NC / 4;             // 16-byte loads per lane per tile
+  // bf16 PV on v_dot2_f32_bf16: a lane holds NI tokens of the same dims, paired up
+  static constexpr bool DOT2_PV = (EB == 2) && (NI >= 2);
+  // blocks in flight per wave (register ring)
+  // (three where the registers allow: 4-wave items, up to 512 VGPRs per lane;
+  // the 8-wave items of the mixed kernel have 256 and keep two)
+  static constexpr int PF = (EB == 2 && G <= 4 && D <= 128 && NW == 4) ? 3 : 2;
+  static constexpr int KST = NW * TILE;         // K staging, all waves
+  static constexpr int RED = NW * TPI * G * D * 4;  // end-of-item reduction
+  static constexpr int AREA = KST > RED ? KST : RED;
+  static constexpr int SMEM = AREA + NW * 16 * G * 4 + NW * G * 8;
+  static_assert(NC >= 4 && NC <= 32, "row of 64..512 bytes");
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "G in {1,2,4,8}");
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_new;  // fused append: [B][hkv][D] new K/V at position ctx-1, or null
+  const void* v_new;
+  const void* kc;
+  const void* vc;
+  const int32_t* bt;
+  const int32_t* ctx_lens;
+  void* out;
+  float* ws_o;        // [B*Hq][n_part][D]
+  float2* ws_ml;      // [B*Hq][n_part]
+  int32_t* err;
+  int32_t hkv;
+  int32_t n_seqs;     // B
+  int32_t num_blocks;
+  int32_t max_blocks;
+  int32_t max_ctx;
+  int32_t part_blocks;
+  int32_t n_part;
+  float scale_log2;   // softmax scale * log2(e)
+};
+
+// Context length the kernels use: clamped to what the grid and table cover.
+__device__ __forceinline__ int effective_ctx(const DecodeArgs& a, int b, bool report) {
+  int ctx = a.ctx_lens[b];
+  const int cap = min(a.max_ctx, a.max_blocks * 16);
+  if (ctx > cap || ctx < 0) {
+    if (report) flag_error(a.err, KVC_DEVERR_CONTEXT);
+    ctx = ctx < 0 ? 0 : cap;
+  }
+  return ctx;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out(void* out, size_t idx, float x);
+template <>
+__device__ __forceinline__ void store_out<float>(void* out, size_t idx, float x) {
+  reinterpret_cast<float*>(out)[idx] = x;
+}
+template <>
+__device__ __forceinline__ void store_out<bf16_tag>(void* out, size_t idx, float x) {
+  reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)f32_to_bf16_bits(x);
+}
+
+// Dot product of one 16-byte chunk pair, 4 independent partial sums.
+template <typename T>
+__device__ __forceinline__ void chunk_dot(const u32x4& k, const u32x4& q, float (&s)[4]);
+template <>
+__device__ __forceinline__ void chunk_dot<bf16_tag>(const u32x4& k, const u32x4& q, float (&s)[4]) {
+  s[0] = dot2_bf16(k.x, q.x, s[0]);
+  s[1] = dot2_bf16(k.y, q.y, s[1]);
+  s[2] = dot2_bf16(k.z, q.z, s[2]);
+  s[3] = dot2_bf16(k.w, q.w, s[3]);
+}
+template <>
+__device__ __forceinline__ void chunk_dot<float>(const u32x4& k, const u32x4& q, float (&s)[4]) {
+  s[0] = fmaf(__uint_as_float(k.x), __uint_as_float(q.x), s[0]);
+  s[1] = fmaf(__uint_as_float(k.y), __uint_as_float(q.y), s[1]);
+  s[2] = fmaf(__uint_as_float(k.z), __uint_as_float(q.z), s[2]);
+  s[3] = fmaf(__uint_as_float(k.w), __uint_as_float(q.w), s[3]);
+}
+
+// Unpack a 16-byte chunk into CE fp32 values.
+template <typename T, int CE>
+__device__ __forceinline__ void unpack(const u32x4& v, float (&x)[CE]);
+template <>
+__device__ __forceinline__ void unpack<bf16_tag, 8>(const u32x4& v, float (&x)[8]) {
+  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+  x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+  x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+template <>
+__device__ __forceinline__ void unpack<float, 4>(const u32x4& v, float (&x)[4]) {
+  x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+  x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+}
+
+// One work item: partition `part` of sequence b for kv head kvh, run by the
+// NW waves of the calling workgroup (every thread calls it, tid = its thread
+// index; smem holds at least DecodeShape<T, D, G, NW>::SMEM bytes). A
+// sequence that fits one partition gets its normalised rows written;
+// otherwise the item writes its partial (m, l, acc) for decode_merge_kernel.
+// A partition holds at most MAX_PART blocks, unless WHOLE: then the waves walk
+// it in ranges of MAX_PART blocks, carrying their softmax state from one range
+// to the next (the mixed-batch kernel gives a whole sequence to one item).
+// FUSE = false compiles the fused append out (the caller has written the new
+// token's K/V already).
+template <typename T, int D, int G, int NW, bool WHOLE = false, bool FUSE = true>
+__device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b, int part,
+                                            uint8_t* smem, int tid = threadIdx.x) {
+  using S = DecodeShape<T, D, G, NW>;
+  const int lane = tid & 63;
+  // the wave index is uniform across the wave; saying so keeps every buffer
+  // descriptor and loop bound in scalar registers (no per-lane waterfall)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hq_all = a.hkv * G;
+
+  const int ctx = effective_ctx(a, b, part == 0 && kvh == 0 && tid == 0);
+  const int nblk = (ctx + 15) >> 4;
+  const int n_used = nblk > 0 ? (nblk + a.part_blocks - 1) / a.part_blocks : 1;
+  if (part >= n_used) return;
+  if (ctx == 0) {
+    for (int o = tid; o < G * D; o += NW * 64)
+      store_out<T>(a.out, ((size_t)b * hq_all + kvh * G) * D + o, 0.f);
+    return;
+  }
+  const int blk_end = min(part * a.part_blocks + a.part_blocks, nblk);
+  int blk0 = part * a.part_blocks;   // first block of the range being walked
+
+  uint8_t* kst = smem + w * S::TILE;
+  float* plds = reinterpret_cast<float*>(smem + S::AREA) + w * 16 * G;
+  uint16_t* p16 = reinterpret_cast<uint16_t*>(plds);          // bf16 weight pairs (DOT2_PV)
+  const uint32_t* p32 = reinterpret_cast<const uint32_t*>(plds);
+  float2* ml = reinterpret_cast<float2*>(smem + S::AREA + NW * 16 * G * 4);
+
+  // QK layout: lane -> (head h, token slot tt, half qh of the head dim). The two
+  // lanes of a pair (qh = 0, 1) hold the two halves of the query row and add
+  // their partial dot products with one DPP step.
+  const int h = lane / S::LPH, qh = (lane % S::LPH) % S::QS, tt = (lane % S::LPH) / S::QS;
+  const bool active = h < G;
+  u32x4 qv[S::NCQ];
+  {
+    const int hq = kvh * G + (active ? h : 0);
+    const u32x4* qp = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const uint8_t*>(a.q) + ((size_t)b * hq_all + hq) * S::RB);
+#pragma unroll
+    for (int c = 0; c < S::NCQ; ++c) qv[c] = qp[qh * S::NCQ + c];
+  }
+
+  const int32_t* bt_row = a.bt + (size_t)b * a.max_blocks;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kc);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vc);
+
+  // This wave's blocks of the range and their ids, one per lane (a range has
+  // at most NW x 64 blocks): inside the loop they are picked with v_readlane,
+  // so no block-table load sits behind the prefetch ring in the in-order load
+  // counter.
+  int n_my = 0;
+  int32_t my_blk = -1;
+  auto start_range = [&] {
+    const int end = WHOLE ? min(blk0 + S::MAX_PART, blk_end) : blk_end;
+    n_my = (end - blk0 > w) ? (end - blk0 - w + NW - 1) / NW : 0;
+    my_blk = lane < n_my ? bt_row[blk0 + w + lane * NW] : -1;
+  };
+
+  // Issue the loads of this wave's i-th block into (kb, vb).
+  auto issue = [&](u32x4 (&kb)[S::NI], u32x4 (&vb)[S::NI], int i) {
+    size_t off = 0;
+    uint32_t bytes = 0;
+    if (i < n_my) {
+      const int blk = __builtin_amdgcn_readlane(my_blk, i);
+      if ((unsigned)blk < (unsigned)a.num_blocks) {
+        off = ((size_t)blk * a.hkv + kvh) * S::TILE;
+        bytes = S::TILE;
+      } else if (lane == 0) {
+        flag_error(a.err, KVC_DEVERR_BLOCK_ID);
+      }
+    }
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + off, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + off, bytes);
+#pragma unroll
+    for (int j = 0; j < S::NI; ++j) kb[j] = buffer_load16_stream(rk, (uint32_t)(j * 64 + lane) * 16u);
+#pragma unroll
+    for (int j = 0; j < S::NI; ++j) vb[j] = buffer_load16_stream(rv, (uint32_t)(j * 64 + lane) * 16u);
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[G][S::CE];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int e = 0; e < S::CE; ++e) acc[hh][e] = 0.f;
+
+  // Fused append. Every load of a tile gives lane `lane` chunk (lane % NC) of
+  // some token, so each lane needs one 16-byte chunk of the new row; it is read
+  // here, before the pipelined loop (memory operations inside the loop would
+  // make the compiler wait on the whole prefetch ring), substituted in
+  // registers when the last block is processed, and stored to the cache after
+  // the loop. Only the workgroup whose partition holds the last block does so.
+  const bool fuse = FUSE && a.k_new != nullptr && part == n_used - 1;
+  const int t_new = (ctx - 1) & 15;
+  u32x4 k_new_c = u32x4{0u, 0u, 0u, 0u}, v_new_c = u32x4{0u, 0u, 0u, 0u};
+  if (fuse) {
+    const size_t src = ((size_t)b * a.hkv + kvh) * S::RB + (lane % S::NC) * 16;
+    k_new_c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.k_new) + src);
+    v_new_c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.v_new) + src);
+  }
+  // One block. TAIL marks the sequence's last block, the only one that can be
+  // partial or hold the appended token; every other block skips the masking
+  // and substitution code entirely.
+  auto process = [&](auto tail_tag, u32x4 (&kb)[S::NI], u32x4 (&vb)[S::NI], int i) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const int lb = blk0 + w + i * NW;
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int j = 0; j < S::NI; ++j) {
+        const int tk = (j * 64 + lane) / S::NC;
+        if (fuse && tk == t_new) {
+          kb[j] = k_new_c;
+          vb[j] = v_new_c;
+        }
+        if (lb * 16 + tk >= ctx) vb[j] = u32x4{0u, 0u, 0u, 0u};   // unwritten rows may hold NaN
+      }
+    }
+    // K tile -> LDS, chunk c of token t at chunk slot c ^ (t % NC)
+#pragma unroll
+    for (int j = 0; j < S::NI; ++j) {
+      const int ci = j * 64 + lane, tk = ci / S::NC, c = ci % S::NC;
+      *reinterpret_cast<u32x4*>(kst + tk * S::RB + ((c ^ (tk % S::NC)) << 4)) = kb[j];
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    float s[S::SPL];
+#pragma unroll
+    for (int sl = 0; sl < S::SPL; ++sl) {
+      const int t = tt + S::TPS * sl;
+      float part_s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < S::NCQ; ++cc) {
+        const int c = qh * S::NCQ + cc;
+        const u32x4 kk = *reinterpret_cast<const u32x4*>(kst + t * S::RB + ((c ^ (t % S::NC)) << 4));
+        chunk_dot<T>(kk, qv[cc], part_s);
+      }
+      float dot = (part_s[0] + part_s[1]) + (part_s[2] + part_s[3]);
+      dot += dpp_f<kQuadXor1>(dot);                  // the other half of the head dim
+      const bool valid = active && (!TAIL || lb * 16 + t < ctx);
+      s[sl] = valid ? dot * a.scale_log2 : -INFINITY;
+    }
+
+    // online softmax over this block's tokens, per head (each token sits in
+    // both lanes of its pair: harmless for the max, counted once in the sum)
+    float mx = s[0];
+#pragma unroll
+    for (int sl = 1; sl < S::SPL; ++sl) mx = fmaxf(mx, s[sl]);
+    mx = group_max<S::LPH>(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_safe);
+    float p[S::SPL], ps = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < S::SPL; ++sl) {
+      p[sl] = __builtin_amdgcn_exp2f(s[sl] - m_safe);
+      // bf16 PV multiplies by bf16 weights: round once here so that the
+      // normaliser l sums exactly the weights the numerator uses
+      if constexpr (S::DOT2_PV) p[sl] = __uint_as_float(f32_to_bf16_bits(p[sl]) << 16);
+      ps += (qh == 0) ? p[sl] : 0.f;
+    }
+    ps = group_sum<S::LPH>(ps);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    if (active && qh == 0) {
+#pragma unroll
+      for (int sl = 0; sl < S::SPL; ++sl) {
+        const int t = tt + S::TPS * sl;
+        if constexpr (S::DOT2_PV) {
+          // packed bf16 pairs in PV order: token t = j*TPI + r sits in pair
+          // (j/2)*TPI + r, low half for even j
+          const int jt = t / S::TPI, r = t % S::TPI;
+          p16[((jt >> 1) * S::TPI + r) * (2 * G) + 2 * h + (jt & 1)] =
+              (uint16_t)(__float_as_uint(p[sl]) >> 16);
+        } else {
+          plds[t * G + h] = p[sl];
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // rescale the accumulators when a running max moved (rare after the first blocks)
+    float al[G];
+    bool moved = false;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      al[hh] = readlane_f(alpha, hh * S::LPH);
+      moved |= (al[hh] != 1.f);
+    }
+    if (__builtin_expect(moved, 0)) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < S::CE; ++e) acc[hh][e] *= al[hh];
+    }
+
+    // PV: lane owns chunk (lane % NC) of tokens j*TPI + lane / NC, j < NI
+    if constexpr (S::DOT2_PV) {
+      // tokens of loads (2m, 2m+1) form a pair; one v_dot2 per (head, dim) and pair
+#pragma unroll
+      for (int m = 0; m < S::NI / 2; ++m) {
+        const int pr = m * S::TPI + lane / S::NC;
+        const u32x4 va = vb[2 * m], vbb = vb[2 * m + 1];
+        uint32_t pp[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) pp[hh] = p32[pr * G + hh];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t xlo = __builtin_amdgcn_perm(vbb[k], va[k], 0x05040100u);
+          const uint32_t xhi = __builtin_amdgcn_perm(vbb[k], va[k], 0x07060302u);
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            acc[hh][2 * k] = dot2_bf16(pp[hh], xlo, acc[hh][2 * k]);
+            acc[hh][2 * k + 1] = dot2_bf16(pp[hh], xhi, acc[hh][2 * k + 1]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < S::NI; ++j) {
+        const int tv = j * S::TPI + lane / S::NC;
+        float pv[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) pv[hh] = plds[tv * G + hh];
+        float x[S::CE];
+        unpack<T, S::CE>(vb[j], x);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+          for (int e = 0; e < S::CE; ++e) acc[hh][e] = fmaf(pv[hh], x[e], acc[hh][e]);
+      }
+    }
+  };
+
+  for (;;) {
+    start_range();
+    // Ring of PF blocks in flight; a slot is refilled right after it is used.
+    // A wave's blocks ascend, so only its last step can be the sequence's last
+    // block: the loop runs the plain path only and the last step is peeled.
+    u32x4 kb[S::PF][S::NI], vb[S::PF][S::NI];
+#pragma unroll
+    for (int u = 0; u < S::PF; ++u) issue(kb[u], vb[u], u);
+    const int n_main = n_my > 0 ? n_my - 1 : 0;
+    for (int i = 0; i < n_main; i += S::PF) {
+#pragma unroll
+      for (int u = 0; u < S::PF; ++u) {
+        if (i + u < n_main) {
+          process(std::false_type{}, kb[u], vb[u], i + u);
+          // keep the refill of this slot after its use: hoisting the loads
+          // above the PV products would force a register copy of the tile
+          __builtin_amdgcn_sched_barrier(0);
+          issue(kb[u], vb[u], i + u + S::PF);
+        }
+      }
+    }
+    if (n_my > 0) {
+      const int last = n_my - 1, slot = last % S::PF;
+      const bool tail = blk0 + w + last * NW == nblk - 1;
+#pragma unroll
+      for (int u = 0; u < S::PF; ++u) {
+        if (u == slot) {
+          if (tail)
+            process(std::true_type{}, kb[u], vb[u], last);
+          else
+            process(std::false_type{}, kb[u], vb[u], last);
+        }
+      }
+    }
+    if constexpr (!WHOLE) break;
+    blk0 += S::MAX_PART;
+    if (blk0 >= blk_end) break;
+  }
+
+  // fused append: write the new token's row (lanes 0..NC-1: K, NC..2NC-1: V)
+  if (fuse && w == 0 && lane < 2 * S::NC) {
+    const int blk = bt_row[nblk - 1];
+    if ((unsigned)blk < (unsigned)a.num_blocks) {
+      const size_t dst = (((size_t)blk * a.hkv + kvh) * 16 + t_new) * S::RB + (lane % S::NC) * 16;
+      uint8_t* base = const_cast<uint8_t*>(lane < S::NC ? kbase : vbase);
+      *reinterpret_cast<u32x4*>(base + dst) = lane < S::NC ? k_new_c : v_new_c;
+    }
+  }
+
+  // merge the four wave states
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);   // [NW][TPI][G][D]
+  {
+    const int sub = lane / S::NC, cc = lane % S::NC;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float* dst = red + ((w * S::TPI + sub) * G + hh) * D + cc * S::CE;
+#pragma unroll
+      for (int e = 0; e < S::CE; e += 4)
+        *reinterpret_cast<f32x4*>(dst + e) = f32x4{acc[hh][e], acc[hh][e + 1], acc[hh][e + 2], acc[hh][e + 3]};
+    }
+    if (active && lane % S::LPH == 0) ml[w * G + h] = make_float2(m_run, l_run);
+  }
+  __syncthreads();
+  for (int o = tid; o < G * D; o += NW * 64) {
+    const int hh = o / D, d = o % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, ml[ww * G + hh].x);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float2 st = ml[ww * G + hh];
+      const float f = (st.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.x - M);
+      float sum = 0.f;
+#pragma unroll
+      for (int sub = 0; sub < S::TPI; ++sub) sum += red[((ww * S::TPI + sub) * G + hh) * D + d];
+      L += st.y * f;
+      A += sum * f;
+    }
+    const size_t row = (size_t)b * hq_all + kvh * G + hh;
+    if (n_used == 1) {
+      store_out<T>(a.out, row * D + d, A / L);
+    } else {
+      a.ws_o[(row * a.n_part + part) * D + d] = A;
+      if (d == 0) a.ws_ml[row * a.n_part + part] = make_float2(M, L);
+    }
+  }
+}
+
+}  // namespace kvc

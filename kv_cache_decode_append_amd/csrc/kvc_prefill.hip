@@ -1,661 +1,26 @@
 // Chunked-prefill attention: write a prompt chunk's K/V into the paged cache,
 // then causal attention of every chunk position over the cached prefix and the
-// chunk's own positions up to itself.
-//
-// Prefill runs the prompt in parallel and is mostly matrix-matrix work
-// (aiwithghost.com "KV cache and continuous batching: 1,000 people ask AI",
-// section "What does a KV cache keep?"); it is capped at a fixed token budget
-// per step so decode waits at most one chunk (gouthm.com "The KV cache is not
-// your bottleneck", section "The fix that mattered"), and it can start after a
-// prefix whose K/V are already cached (daviddominguez.dev "The KV cache and
-// prefix caching", section "A prefix already in the cache can skip its
-// prefill"). This is the one dense contraction of the path, so it runs on MFMA.
-//
-// Tiling (one workgroup = 8 waves = 256 query rows of one kv head):
-//   row r <-> (position qt*MP + r / G, query head kvh*G + r % G), MP = 256 / G,
-//   so the G query heads that share a K/V head share every K/V tile.
-//   Keys are walked in tiles of 64 (four 16-token blocks through the block
-//   table). Per tile and wave (2 row tiles of 16):
-//     S^T[key][row] = K . Q^T          MFMA, A = K from LDS, B = Q from registers
-//     online softmax per row            each lane owns one row (lane % 16)
-//     O^T[dim][row] += V^T . P^T       MFMA, A = V^T from LDS, B = P from the S^T
-//                                       registers (no transpose of P needed)
-//   bf16: v_mfma_f32_16x16x32_bf16 (V staged transposed in LDS);
-//   fp32: v_mfma_f32_16x16x4_f32 (V read row-major, one element per lane).
-//   The reduction order inside an MFMA over keys is a permutation of the keys
-//   (key 16m + 4g + i for lane group g); A and B use the same permutation.
-//   The three steps are software-pipelined across key tiles so that the
-//   softmax of one tile overlaps the PV product of the previous one.
-
-#include <math.h>
+// chunk's own positions up to itself (the work item is in kvc_prefill_item.h),
+// with optional key-range splits and their merge kernel, and the host entry
+// points.
 
 #include <algorithm>
 
-#include "kvc_append.h"
-#include "kvc_device.h"
 #include "kvc_host.h"
+#include "kvc_prefill_item.h"
 
 namespace kvc {
 
-constexpr int kPfWaves = 8;
-constexpr int kPfThreads = kPfWaves * 64;
-constexpr int kRowTiles = 2;                        // 16-row tiles per wave
-constexpr int kRows = kPfWaves * kRowTiles * 16;    // 256 query rows per workgroup
-constexpr int kKeyTile = 64;                        // keys per staged tile
-constexpr int kWaitVmcnt0 = 0x0F70;                 // s_waitcnt vmcnt(0) (expcnt, lgkmcnt: no wait)
-constexpr uint32_t kBf16OnePair = 0x3F803F80u;      // bf16 (1, 1)
-
-template <typename T> struct PfMfma;
-template <> struct PfMfma<bf16_tag> {
-  static constexpr int K = 32;                      // reduction depth per instruction
-  using Frag = bf16x8_t;
-  __device__ static f32x4 mma(const Frag& a, const Frag& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-template <> struct PfMfma<float> {
-  static constexpr int K = 4;
-  using Frag = float;
-  __device__ static f32x4 mma(const Frag& a, const Frag& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-  }
-};
-
-// Softmax weights of one key tile as the PV product consumes them: bf16 pairs
-// packed as MFMA B fragments, or fp32 one per (key tile, row tile, element).
-template <bool BF16> struct PfP;
-template <> struct PfP<true> { struct Tile { u32x4 v[2][kRowTiles]; }; };
-template <> struct PfP<false> { struct Tile { float v[4][kRowTiles][4]; }; };
-
-template <typename T, int D, int G>
-struct PfShape {
-  static constexpr int EB = ElemBytes<T>::value;
-  static constexpr int RB = D * EB;                 // bytes per K row in LDS
-  static constexpr int NC = RB / 16;                // 16-byte chunks per row
-  static constexpr int MP = kRows / G;              // positions per workgroup
-  static constexpr int KS = D / PfMfma<T>::K;       // k-steps over head_dim
-  static constexpr int DT = D / 16;                 // output dim tiles
-  static constexpr bool BF16 = (EB == 2);
-  static constexpr int VT_STRIDE = kKeyTile + 8;    // padded V^T row (elements), bf16 only
-  static constexpr int K_UNITS = kKeyTile * NC;     // 16-byte chunks of a K tile
-  static constexpr int KPT = (K_UNITS + kPfThreads - 1) / kPfThreads;
-  // V staging units: bf16 = (key pair, chunk) transposed on the way in; fp32 = chunk
-  static constexpr int V_UNITS = BF16 ? (kKeyTile / 2) * NC : K_UNITS;
-  static constexpr int VPT = (V_UNITS + kPfThreads - 1) / kPfThreads;
-  static constexpr int VCH = BF16 ? 2 : 1;          // chunks per V unit
-  static constexpr int K_LDS = kKeyTile * RB;
-  static constexpr int V_LDS = BF16 ? D * VT_STRIDE * 2 : kKeyTile * RB;
-  static constexpr int TILES = 2 * K_LDS + 2 * V_LDS;   // two K and two V tile buffers
-  // pool rows of the blocks a workgroup reads, kept in LDS: 8,192 blocks
-  // (131,072 keys) where the tile buffers leave room, else 2,048
-  static constexpr int BT_CACHE = TILES <= 96 * 1024 ? 8192 : 2048;
-  static constexpr int SMEM = TILES + BT_CACHE * 4;
-  static_assert(kRows % G == 0, "G divides the row count");
-};
-
-struct PrefillArgs {
-  const void* q;
-  const void* kc;
-  const void* vc;
-  const int32_t* cu;
-  const int32_t* prefix;
-  const int32_t* bt;
-  void* out;
-  int32_t* err;
-  int32_t hkv;
-  int32_t num_blocks;
-  int32_t max_blocks;
-  int32_t total;
-  int32_t max_chunk;
-  int32_t n_qt;       // query tiles per sequence (grid decomposition)
-  int32_t n_split;    // key-range splits per query tile (1: no split, rows written directly)
-  int32_t split_tiles;  // key tiles per split
-  int32_t n_work;     // n_qt * n_split * hkv * n_seqs
-  float scale_log2;
-  float* ws_o;        // split partials: [total][Hq][n_split][D] fp32, unnormalised
-  float2* ws_ml;      // [total][Hq][n_split] (running max in log2 units, row sum)
-};
-
-template <typename T>
-__device__ __forceinline__ void store4(void* out, size_t idx, const f32x4& v, float inv);
-template <>
-__device__ __forceinline__ void store4<float>(void* out, size_t idx, const f32x4& v, float inv) {
-  *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + idx) =
-      f32x4{v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv};
-}
-template <>
-__device__ __forceinline__ void store4<bf16_tag>(void* out, size_t idx, const f32x4& v, float inv) {
-  *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + idx) =
-      u32x2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
-}
-
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillArgs a) {
-  using S = PfShape<T, D, G>;
-  using M = PfMfma<T>;
-  using Frag = typename M::Frag;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
-  int32_t* bt_lds = reinterpret_cast<int32_t*>(smem + S::TILES);
-
+  __shared__ __attribute__((aligned(16))) uint8_t smem[PfShape<T, D, G>::SMEM];
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
   // each XCD a contiguous run of work items; the query tiles of one (sequence,
   // kv head) then share one L2 while they sweep the same keys.
   const int per_xcd = gridDim.x / 8;
   const int work = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (work >= a.n_work) return;
-  const int qt = work % a.n_qt;
-  const int sp = (work / a.n_qt) % a.n_split;
-  const int kvh = (work / (a.n_qt * a.n_split)) % a.hkv;
-  const int s = work / (a.n_qt * a.n_split * a.hkv);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = lane >> 4, l16 = lane & 15;
-  const int t0 = a.cu[s];
-  const int C = a.cu[s + 1] - t0;
-  const int p0 = a.prefix[s];
-  const int pos_lo = qt * S::MP;
-  if (!chunk_ok(t0, C, p0, a.total, a.max_chunk)) {
-    if (qt == 0 && sp == 0 && kvh == 0 && tid == 0) flag_error(a.err, KVC_DEVERR_CONTEXT);
-    return;
-  }
-  if (pos_lo >= C) return;
-  const int kv_len = p0 + C;                           // keys that exist after the write
-  const int last_pos = p0 + min(pos_lo + S::MP, C) - 1;
-  const int hq_all = a.hkv * G;
-  // this workgroup's key tiles: [t_begin, t_end) of the ones its rows reach
-  const int t_begin = sp * a.split_tiles;
-  const int t_end = min(last_pos / kKeyTile + 1, t_begin + a.split_tiles);
-  if (sp == a.n_split - 1 && last_pos / kKeyTile + 1 > t_begin + a.split_tiles && tid == 0)
-    flag_error(a.err, KVC_DEVERR_CONTEXT);             // keys past max_context_len
-
-  if (t_begin >= t_end) {
-    // a split past this query tile's keys: an empty partial for each of its rows
-    const int rows = min(S::MP, C - pos_lo) * G;
-    for (int r = tid; r < rows; r += kPfThreads) {
-      const size_t pr = ((size_t)(t0 + pos_lo + r / G) * hq_all + kvh * G + r % G) * a.n_split + sp;
-      a.ws_ml[pr] = float2{-INFINITY, 0.f};
-      for (int d = 0; d < D; d += 4)
-        *reinterpret_cast<f32x4*>(a.ws_o + pr * D + d) = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    return;
-  }
-  const int32_t* bt_row = a.bt + (size_t)s * a.max_blocks;
-
-  // The pool row (block id * Hkv + kv head) of every block this workgroup
-  // reads, validated once and cached in LDS; -1 for a block that holds no key
-  // or has an id outside the pool. Contract violations are collected per lane
-  // and flagged once at the end.
-  const int nb_need = (min(kv_len, t_end * kKeyTile) + 15) / 16;
-  int bad = 0;
-  auto pool_row = [&](int lb) -> int {
-    if (lb >= nb_need) return -1;
-    if (lb >= a.max_blocks) {
-      bad |= KVC_DEVERR_CONTEXT;
-      return -1;
-    }
-    const int blk = bt_row[lb];
-    if ((unsigned)blk >= (unsigned)a.num_blocks) {
-      bad |= KVC_DEVERR_BLOCK_ID;
-      return -1;
-    }
-    return blk * a.hkv + kvh;
-  };
-  const int lb0 = 4 * t_begin;                         // cache entry 0 = block lb0
-  for (int i = tid; i < min(4 * (t_end - t_begin + 1), S::BT_CACHE); i += kPfThreads)
-    bt_lds[i] = pool_row(lb0 + i);
-
-  // rows owned by this lane: r = w*32 + n*16 + l16
-  int row_pos[kRowTiles];                              // absolute position (clamped)
-  bool row_ok[kRowTiles];
-  Frag qf[kRowTiles][S::KS];
-#pragma unroll
-  for (int n = 0; n < kRowTiles; ++n) {
-    const int r = w * (kRowTiles * 16) + n * 16 + l16;
-    const int pl = pos_lo + r / G, h = r % G;
-    row_ok[n] = pl < C;
-    row_pos[n] = p0 + min(pl, C - 1);
-    const size_t qrow = ((size_t)(t0 + min(pl, C - 1)) * hq_all + kvh * G + h) * D;
-#pragma unroll
-    for (int kk = 0; kk < S::KS; ++kk) {
-      if constexpr (S::BF16) {
-        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + qrow + kk * 32 + g * 8;
-        qf[n][kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(qp));
-      } else {
-        qf[n][kk] = reinterpret_cast<const float*>(a.q)[qrow + kk * 4 + g];
-      }
-    }
-  }
-
-  f32x4 o[kRowTiles][S::DT];
-  float m_run[kRowTiles], l_run[kRowTiles];
-#pragma unroll
-  for (int n = 0; n < kRowTiles; ++n) {
-    m_run[n] = -INFINITY;
-    l_run[n] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < S::DT; ++dt) o[n][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  __syncthreads();                                     // block-id cache ready
-
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kc);
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vc);
-  // Pool row of logical block lb of a tile that `cached` says lies inside the
-  // LDS cache (the same for the whole tile). Past the cache the row is read
-  // and checked here; that read waits for itself inside its branch, so the
-  // common path never waits for an outstanding K/V load.
-  const __amdgpu_buffer_rsrc_t bt_rsrc = make_rsrc(bt_row, (uint32_t)a.max_blocks * 4u);
-  auto block_row = [&](int lb, bool cached) -> int {
-    if (cached) return bt_lds[lb - lb0];
-    int r = -1;
-    if (lb < nb_need) {
-      if (lb >= a.max_blocks) {
-        bad |= KVC_DEVERR_CONTEXT;
-      } else {
-        const int blk = __builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, lb * 4, 0, 0);
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        if ((unsigned)blk < (unsigned)a.num_blocks)
-          r = blk * a.hkv + kvh;
-        else
-          bad |= KVC_DEVERR_BLOCK_ID;
-      }
-    }
-    return r;
-  };
-  // 16 bytes (chunk c) of key `key` of tile kt. An absent key loads from the
-  // pool's first row (always valid) and is zeroed when stored to LDS, so no
-  // wait for the load lands here.
-  struct Row16 { int64_t off; bool ok; };
-  auto locate = [&](int kt, int key, bool cached) -> Row16 {
-    const int r = block_row(kt * 4 + (key >> 4), cached);
-    const bool ok = r >= 0 && kt * kKeyTile + key < kv_len;
-    return {ok ? (int64_t)r * (16 * S::RB) + (key & 15) * S::RB : 0, ok};
-  };
-  auto zero_unless = [](bool ok, const u32x4& v) { return ok ? v : u32x4{0u, 0u, 0u, 0u}; };
-
-  // Register staging of K and V tiles. K runs two tiles ahead of V (QK^T of
-  // tile k+1 is computed before PV of tile k), so each is loaded on its own.
-  constexpr bool kAllK = S::K_UNITS % kPfThreads == 0;   // every thread has every K unit
-  constexpr bool kAllV = S::V_UNITS % kPfThreads == 0;
-  u32x4 kr[S::KPT], vr[S::VPT][S::VCH];
-  bool kok[S::KPT], vok[S::VPT][S::VCH];
-  // A wave's K units cover 64 / NC <= 16 consecutive keys starting at a
-  // multiple of 64 / NC, so they sit in one block: its base is a scalar, and
-  // the lane's offset inside the block does not change between tiles. A unit
-  // of an absent block reads inside the pool's first block (always valid).
-  static_assert(16 % (64 / S::NC) == 0, "a wave's K rows stay in one block");
-  auto load_k = [&](int kt) {
-    const bool cached = 4 * (kt - t_begin) < S::BT_CACHE;
-#pragma unroll
-    for (int j = 0; j < S::KPT; ++j) {
-      const int ci = tid + j * kPfThreads;
-      const bool has = kAllK || ci < S::K_UNITS;
-      const int key = has ? ci / S::NC : 0;
-      const int r = __builtin_amdgcn_readfirstlane(
-          block_row(kt * 4 + __builtin_amdgcn_readfirstlane(key >> 4), cached));
-      const uint8_t* base = kbase + (r >= 0 ? (int64_t)r * (16 * S::RB) : 0);
-      kok[j] = has && r >= 0 && kt * kKeyTile + key < kv_len;
-      kr[j] = *reinterpret_cast<const u32x4*>(base + (key & 15) * S::RB + (ci % S::NC) * 16);
-    }
-  };
-  auto load_v = [&](int kt) {
-    const bool cached = 4 * (kt - t_begin) < S::BT_CACHE;
-#pragma unroll
-    for (int j = 0; j < S::VPT; ++j) {
-      const int u = tid + j * kPfThreads;
-      const bool has = kAllV || u < S::V_UNITS;
-#pragma unroll
-      for (int x = 0; x < S::VCH; ++x) {
-        // bf16 unit u = (key pair u % 32, chunk u / 32): a wave's transposing
-        // stores then cover all 32 key pairs and hit 64 distinct LDS banks
-        const int key = !has ? 0 : S::BF16 ? 2 * (u % (kKeyTile / 2)) + x : u / S::NC;
-        const int c = S::BF16 ? u / (kKeyTile / 2) : u % S::NC;
-        const Row16 rw = locate(kt, key, cached);
-        vok[j][x] = has && rw.ok;
-        vr[j][x] = *reinterpret_cast<const u32x4*>(vbase + rw.off + c * 16);
-      }
-    }
-  };
-  auto store_k = [&](uint8_t* k_lds) {
-#pragma unroll
-    for (int j = 0; j < S::KPT; ++j) {
-      const int ci = tid + j * kPfThreads;
-      if (kAllK || ci < S::K_UNITS) {
-        const int key = ci / S::NC, c = ci % S::NC;
-        *reinterpret_cast<u32x4*>(k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)) =
-            zero_unless(kok[j], kr[j]);
-      }
-    }
-  };
-  auto store_v = [&](uint8_t* v_lds) {
-#pragma unroll
-    for (int j = 0; j < S::VPT; ++j) {
-      const int u = tid + j * kPfThreads;
-      if (!kAllV && u >= S::V_UNITS) continue;
-      const u32x4 v0 = zero_unless(vok[j][0], vr[j][0]);
-      const u32x4 v1 = zero_unless(vok[j][S::VCH - 1], vr[j][S::VCH - 1]);
-      if constexpr (S::BF16) {
-        // keys (2kp, 2kp+1) x dims 8c..8c+7 -> V^T[dim][2kp .. 2kp+1], one dword per dim
-        const int kp = u % (kKeyTile / 2), c = u / (kKeyTile / 2);
-        uint32_t* vt = reinterpret_cast<uint32_t*>(v_lds);
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          const uint32_t lo = __builtin_amdgcn_perm(v1[wd], v0[wd], 0x05040100u);
-          const uint32_t hi = __builtin_amdgcn_perm(v1[wd], v0[wd], 0x07060302u);
-          vt[((c * 8 + 2 * wd) * S::VT_STRIDE + 2 * kp) / 2] = lo;
-          vt[((c * 8 + 2 * wd + 1) * S::VT_STRIDE + 2 * kp) / 2] = hi;
-        }
-      } else {
-        const int key = u / S::NC, c = u % S::NC;
-        *reinterpret_cast<u32x4*>(v_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)) = v0;
-      }
-    }
-  };
-
-  // ---- S^T = K . Q^T for one key tile: 4 key tiles x kRowTiles row tiles.
-  // The K fragments of key tile m+1 are read from LDS while tile m multiplies.
-  auto load_kf = [&](const uint8_t* k_lds, int m, Frag (&kf)[S::KS]) {
-    const int key = m * 16 + l16;
-#pragma unroll
-    for (int kk = 0; kk < S::KS; ++kk) {
-      if constexpr (S::BF16) {
-        const int c = kk * 4 + g;
-        kf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
-                                                  k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)));
-      } else {
-        const int c = kk;                            // dims 4kk .. 4kk+3, element g
-        kf[kk] = *reinterpret_cast<const float*>(k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4) +
-                                                 g * 4);
-      }
-    }
-  };
-  auto qk = [&](const uint8_t* k_lds, f32x4 (&sacc)[4][kRowTiles]) {
-    if constexpr (S::BF16) {
-      // steps (m, kk); the fragment of step st+kAhead is read while step st
-      // multiplies, and a scheduling fence per step keeps that order
-      constexpr int kSteps = 4 * S::KS, kAhead = 3;
-      bf16x8_t kf[kAhead + 1];
-      auto frag = [&](int st) {
-        const int key = (st / S::KS) * 16 + l16, c = (st % S::KS) * 4 + g;
-        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
-                                                k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)));
-      };
-#pragma unroll
-      for (int st = 0; st < kAhead; ++st) kf[st] = frag(st);
-#pragma unroll
-      for (int st = 0; st < kSteps; ++st) {
-        if (st + kAhead < kSteps) kf[(st + kAhead) % (kAhead + 1)] = frag(st + kAhead);
-        const int m = st / S::KS, kk = st % S::KS;
-#pragma unroll
-        for (int n = 0; n < kRowTiles; ++n)
-          sacc[m][n] = M::mma(kf[st % (kAhead + 1)], qf[n][kk],
-                              kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[m][n]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        Frag kf[S::KS];
-        load_kf(k_lds, m, kf);
-#pragma unroll
-        for (int kk = 0; kk < S::KS; ++kk)
-#pragma unroll
-          for (int n = 0; n < kRowTiles; ++n)
-            sacc[m][n] = M::mma(kf[kk], qf[n][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[m][n]);
-      }
-    }
-  };
-  // causal mask, only for tiles that reach past the smallest row position
-  auto mask = [&](f32x4 (&sacc)[4][kRowTiles], int key0) {
-    if (__builtin_expect(key0 + kKeyTile - 1 > p0 + pos_lo, 0)) {
-#pragma unroll
-      for (int n = 0; n < kRowTiles; ++n)
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (key0 + m * 16 + g * 4 + i > row_pos[n]) sacc[m][n][i] = -INFINITY;
-    }
-  };
-  // ---- online softmax of one tile (lane owns row l16 of each row tile).
-  // Row sums stay per lane (a partial over this lane's keys) until the end;
-  // the running max is reduced across the row every tile.
-  using PTile = typename PfP<S::BF16>::Tile;
-  auto softmax = [&](const f32x4 (&sacc)[4][kRowTiles], PTile& pt, float (&alpha)[kRowTiles]) {
-#pragma unroll
-    for (int n = 0; n < kRowTiles; ++n) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[m][n][i]);
-      mx = rows_max(mx);
-      const float m_new = fmaxf(m_run[n], mx * a.scale_log2);
-      const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-      alpha[n] = __builtin_amdgcn_exp2f(m_run[n] - m_safe);
-      m_run[n] = m_new;
-      float p[4][4];
-      float rs = 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[m][i] = __builtin_amdgcn_exp2f(fmaf(sacc[m][n][i], a.scale_log2, -m_safe));
-          if constexpr (!S::BF16) rs += p[m][i];
-        }
-      if constexpr (S::BF16) {
-        // the row sum adds the bf16 weights the PV product uses
-#pragma unroll
-        for (int mp = 0; mp < 2; ++mp) {
-          pt.v[mp][n] = u32x4{pack_bf16x2(p[2 * mp][0], p[2 * mp][1]),
-                              pack_bf16x2(p[2 * mp][2], p[2 * mp][3]),
-                              pack_bf16x2(p[2 * mp + 1][0], p[2 * mp + 1][1]),
-                              pack_bf16x2(p[2 * mp + 1][2], p[2 * mp + 1][3])};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) rs = dot2_bf16(pt.v[mp][n][q], kBf16OnePair, rs);
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pt.v[m][n][i] = p[m][i];
-      }
-      l_run[n] = fmaf(l_run[n], alpha[n], rs);
-    }
-  };
-  // ---- O^T += V^T . P^T for one tile; V fragments are read one step ahead
-  auto pv = [&](const uint8_t* v_lds, const PTile& pt) {
-    if constexpr (S::BF16) {
-      const uint16_t* vt = reinterpret_cast<const uint16_t*>(v_lds);
-      auto load_vf = [&](int mp, int dt) -> Frag {
-        const uint16_t* rowp = vt + (dt * 16 + l16) * S::VT_STRIDE + mp * 32 + g * 4;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(rowp);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(rowp + 16);
-        return __builtin_bit_cast(bf16x8_t, u32x4{lo[0], lo[1], hi[0], hi[1]});
-      };
-      Frag vf[2];
-      vf[0] = load_vf(0, 0);
-#pragma unroll
-      for (int st = 0; st < 2 * S::DT; ++st) {          // st = (mp, dt)
-        const int mp = st / S::DT, dt = st % S::DT;
-        if (st + 1 < 2 * S::DT) vf[(st + 1) & 1] = load_vf((st + 1) / S::DT, (st + 1) % S::DT);
-#pragma unroll
-        for (int n = 0; n < kRowTiles; ++n)
-          o[n][dt] = M::mma(vf[st & 1], __builtin_bit_cast(bf16x8_t, pt.v[mp][n]), o[n][dt]);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = m * 16 + g * 4 + i;
-#pragma unroll
-          for (int dt = 0; dt < S::DT; ++dt) {
-            const int dim = dt * 16 + l16, c = dim >> 2;
-            const float vf = *reinterpret_cast<const float*>(
-                v_lds + key * S::RB + ((c ^ (key % S::NC)) << 4) + (dim & 3) * 4);
-#pragma unroll
-            for (int n = 0; n < kRowTiles; ++n) o[n][dt] = M::mma(vf, pt.v[m][n][i], o[n][dt]);
-          }
-        }
-    }
-  };
-  // bf16: PV of one tile fused with the softmax of the next, one PV step
-  // (a V fragment times both row tiles) at a time with a slice of the softmax
-  // after it, each step fenced so the vector work stays between the MFMAs.
-  // Softmax units: 0, 1 = partial row max of row tile 0, 1; 2 = max across
-  // the row, new running max and rescale factor; 3 + e = weight e (row tile
-  // e / 16, key tile (e / 4) % 4, element e % 4), packed to bf16 in pairs.
-  auto pv_softmax = [&](const uint8_t* v_lds, const PTile& pt, const f32x4 (&sc)[4][kRowTiles],
-                        PTile& pn, float (&alpha)[kRowTiles]) {
-    if constexpr (S::BF16) {
-      constexpr int kSteps = 2 * S::DT, kAhead = 2;
-      constexpr int kUnits = 3 + 16 * kRowTiles;
-      const uint16_t* vt = reinterpret_cast<const uint16_t*>(v_lds);
-      auto frag = [&](int st) {
-        const int mp = st / S::DT, dt = st % S::DT;
-        const uint16_t* rowp = vt + (dt * 16 + l16) * S::VT_STRIDE + mp * 32 + g * 4;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(rowp);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(rowp + 16);
-        return __builtin_bit_cast(bf16x8_t, u32x4{lo[0], lo[1], hi[0], hi[1]});
-      };
-      float mx[kRowTiles], msafe[kRowTiles], rs[kRowTiles], pw[kRowTiles][4][4];
-      auto unit = [&](int u) {
-        if (u < kRowTiles) {
-          float v = -INFINITY;
-  #pragma unroll
-          for (int m = 0; m < 4; ++m)
-  #pragma unroll
-            for (int i = 0; i < 4; ++i) v = fmaxf(v, sc[m][u][i]);
-          mx[u] = v;
-        } else if (u == kRowTiles) {
-  #pragma unroll
-          for (int n = 0; n < kRowTiles; ++n) {
-            const float m_new = fmaxf(m_run[n], rows_max(mx[n]) * a.scale_log2);
-            msafe[n] = (m_new == -INFINITY) ? 0.f : m_new;
-            alpha[n] = __builtin_amdgcn_exp2f(m_run[n] - msafe[n]);
-            m_run[n] = m_new;
-            rs[n] = 0.f;
-          }
-        } else {
-          const int e = u - kRowTiles - 1, n = e / 16, m = (e / 4) % 4, i = e % 4;
-          pw[n][m][i] = __builtin_amdgcn_exp2f(fmaf(sc[m][n][i], a.scale_log2, -msafe[n]));
-          if (i & 1) {
-            const uint32_t pair = pack_bf16x2(pw[n][m][i - 1], pw[n][m][i]);
-            pn.v[m / 2][n][(m % 2) * 2 + i / 2] = pair;
-            rs[n] = dot2_bf16(pair, kBf16OnePair, rs[n]);   // sum of the weights PV uses
-          }
-        }
-      };
-      bf16x8_t vf[kAhead + 1];
-  #pragma unroll
-      for (int st = 0; st < kAhead; ++st) vf[st] = frag(st);
-  #pragma unroll
-      for (int st = 0; st < kSteps; ++st) {
-        if (st + kAhead < kSteps) vf[(st + kAhead) % (kAhead + 1)] = frag(st + kAhead);
-        const int mp = st / S::DT, dt = st % S::DT;
-  #pragma unroll
-        for (int n = 0; n < kRowTiles; ++n)
-          o[n][dt] = M::mma(vf[st % (kAhead + 1)], __builtin_bit_cast(bf16x8_t, pt.v[mp][n]), o[n][dt]);
-  #pragma unroll
-        for (int u = 0; u < kUnits; ++u)
-          if (u * kSteps / kUnits == st) unit(u);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-  #pragma unroll
-      for (int n = 0; n < kRowTiles; ++n) l_run[n] = fmaf(l_run[n], alpha[n], rs[n]);
-    }
-  };
-  auto rescale = [&](const float (&alpha)[kRowTiles]) {
-#pragma unroll
-    for (int n = 0; n < kRowTiles; ++n)
-      if (__builtin_expect(__any(alpha[n] != 1.f), 0)) {   // wave-uniform: skip when no max moved
-#pragma unroll
-        for (int dt = 0; dt < S::DT; ++dt) o[n][dt] *= alpha[n];
-      }
-  };
-
-  // Barrier for LDS hand-off only: waits for this wave's LDS operations, not
-  // for its outstanding global loads (which a full fence would drain).
-  auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-
-  // Software pipeline over key tiles. Iteration kt holds K(kt+1) and V(kt) in
-  // LDS and P(kt) in registers: it multiplies QK^T of tile kt+1 on MFMA, then
-  // PV of tile kt on MFMA while the softmax of tile kt+1 runs on the vector
-  // ALUs, and applies tile kt+1's rescale after PV(kt). K(kt+2) and V(kt+1)
-  // are loaded during the iteration and stored behind it; K and V each have
-  // two LDS buffers, and the barrier closing an iteration publishes the new
-  // tiles after every wave has finished with the ones they overwrite.
-  auto kbuf = [&](int i) { return smem + (i & 1) * S::K_LDS; };
-  auto vbuf = [&](int i) { return smem + 2 * S::K_LDS + (i & 1) * S::V_LDS; };
-  f32x4 sacc[4][kRowTiles];
-  PTile pt;
-  float alpha[kRowTiles];
-  load_k(t_begin);
-  load_v(t_begin);
-  store_k(kbuf(t_begin));
-  store_v(vbuf(t_begin));
-  if (t_end - t_begin > 1) {
-    load_k(t_begin + 1);
-    store_k(kbuf(t_begin + 1));
-  }
-  lds_barrier();
-  qk(kbuf(t_begin), sacc);
-  mask(sacc, t_begin * kKeyTile);
-  softmax(sacc, pt, alpha);                           // o is still zero: no rescale
-  lds_barrier();                                       // K(0) read by every wave
-  for (int kt = t_begin; kt + 1 < t_end; ++kt) {
-    const bool more_k = kt + 2 < t_end;
-    if (more_k) load_k(kt + 2);
-    load_v(kt + 1);
-    qk(kbuf(kt + 1), sacc);
-    mask(sacc, (kt + 1) * kKeyTile);
-    PTile pt_next;
-    if constexpr (S::BF16) {
-      pv_softmax(vbuf(kt), pt, sacc, pt_next, alpha);
-      // the next tile's weights and row sums are computed between the PV
-      // MFMAs; pin them there so they are not sunk past the rescale branch
-#pragma unroll
-      for (int mp = 0; mp < 2; ++mp)
-#pragma unroll
-        for (int n = 0; n < kRowTiles; ++n) asm volatile("" : "+v"(pt_next.v[mp][n]));
-#pragma unroll
-      for (int n = 0; n < kRowTiles; ++n) asm volatile("" : "+v"(l_run[n]));
-    } else {
-      pv(vbuf(kt), pt);
-      softmax(sacc, pt_next, alpha);
-    }
-    rescale(alpha);
-    pt = pt_next;
-    if (more_k) store_k(kbuf(kt));
-    store_v(vbuf(kt + 1));
-    lds_barrier();
-  }
-  pv(vbuf(t_end - 1), pt);
-
-  if (bad) flag_error(a.err, bad);
-
-  // ---- write rows: lane holds dims 16dt + 4g .. +3 of row l16 ----
-  float l_row[kRowTiles];
-#pragma unroll
-  for (int n = 0; n < kRowTiles; ++n) l_row[n] = rows_sum(l_run[n]);   // whole wave, before any exit
-#pragma unroll
-  for (int n = 0; n < kRowTiles; ++n) {
-    if (!row_ok[n]) continue;
-    const int r = w * (kRowTiles * 16) + n * 16 + l16;
-    const int pl = pos_lo + r / G, h = r % G;
-    const size_t row = (size_t)(t0 + pl) * hq_all + kvh * G + h;
-    if (a.n_split == 1) {
-      const float inv = 1.f / l_row[n];
-#pragma unroll
-      for (int dt = 0; dt < S::DT; ++dt) store4<T>(a.out, row * D + dt * 16 + g * 4, o[n][dt], inv);
-    } else {
-      // partial of this key range: unnormalised accumulators, running max, row sum
-      const size_t pr = row * a.n_split + sp;
-#pragma unroll
-      for (int dt = 0; dt < S::DT; ++dt)
-        *reinterpret_cast<f32x4*>(a.ws_o + pr * D + dt * 16 + g * 4) = o[n][dt];
-      if (g == 0) a.ws_ml[pr] = float2{m_run[n], l_row[n]};
-    }
-  }
+  prefill_item<T, D, G>(a, work, smem);
 }
 
 // One wave per (token, query head): combine the key-range partials of a split

@@ -130,3 +130,47 @@ def test_status_strings():
     for s in range(-9, 1):
         assert LIB.kvc_status_string(s)
     assert LIB.kvc_status_string(-99) == b"unknown status"
+
+
+def _mixed(**over):
+    b = kvc._lib._CMixed()
+    for k, v in over.items():
+        setattr(b, k, v)
+    return b
+
+
+def test_mixed_workspace_closed_form():
+    # the queue header, then one int per decode row (rounded up to 256 bytes)
+    assert kvc.mixed_workspace_bytes(0, 0, 32, 8, 128) == 256
+    assert kvc.mixed_workspace_bytes(64, 2048, 32, 8, 128) == 512
+    assert kvc.mixed_workspace_bytes(206, 32000, 32, 8, 128) == 256 + 1024
+    assert kvc.mixed_workspace_bytes(4096, 32000, 32, 8, 128) == 256 + 16384
+    assert kvc.mixed_workspace_bytes(4097, 16, 32, 8, 128) == 0
+    assert kvc.mixed_workspace_bytes(4, 16, 6, 4, 128) == 0
+
+
+def test_mixed_step_rejects_before_launch():
+    c = _cache(num_kv_heads=2, head_dim=32)
+    byref = ctypes.byref(c)
+    ws = kvc.mixed_workspace_bytes(2, 100, 4, 2, 32)
+    dec = dict(n_decode=2, q_decode=1, k_new=1, v_new=1, decode_block_table=1,
+               decode_max_blocks=8, decode_context_lens=1, decode_max_context=100, out_decode=1)
+    f = LIB.kvc_mixed_step_attention
+    assert f(byref, None, 4, 0.1, 1, ws, None) == -1                       # no batch
+    assert f(byref, ctypes.byref(_mixed()), 4, 0.1, None, 0, None) == 0    # nothing to do
+    assert f(byref, ctypes.byref(_mixed(**dec)), 4, 0.1, None, 0, None) == -5   # no workspace
+    assert f(byref, ctypes.byref(_mixed(**dec)), 4, 0.1, 1, ws - 1, None) == -5
+    assert f(byref, ctypes.byref(_mixed(**dict(dec, q_decode=None))), 4, 0.1, 1, ws, None) == -1
+    assert f(byref, ctypes.byref(_mixed(**dict(dec, decode_max_context=129))), 4, 0.1, 1, ws,
+             None) == -2                                                    # beyond 8 blocks
+    assert f(byref, ctypes.byref(_mixed(**dict(dec, n_decode=4097))), 4, 0.1, 1, 1 << 30,
+             None) == -4
+    assert f(byref, ctypes.byref(_mixed(**dec)), 16, 0.1, 1, 1 << 30, None) == -4   # G = 8
+    assert f(byref, ctypes.byref(_mixed(**dec)), 6, 0.1, 1, 1 << 30, None) == -4   # G = 3
+    assert f(byref, ctypes.byref(_mixed(**dec)), 5, 0.1, 1, 1 << 30, None) == -2   # 5 % 2 != 0
+    c64 = _cache(num_kv_heads=2, head_dim=64)
+    assert f(ctypes.byref(c64), ctypes.byref(_mixed(**dec)), 4, 0.1, 1, 1 << 30, None) == -4
+    pf = dict(n_prefill=1, q_prefill=1, k_prefill=1, v_prefill=1, cu_chunk_lens=1, prefix_lens=1,
+              prefill_total_tokens=10, prefill_max_chunk=10, prefill_block_table=1,
+              prefill_max_blocks=4, out_prefill=None)
+    assert f(byref, ctypes.byref(_mixed(**pf)), 4, 0.1, 1, 1 << 30, None) == -1
