@@ -672,6 +672,27 @@ def bench_queue_replay(args):
                                               max_chunk, scale, out=out[:total])
         return run
 
+    mws = torch.zeros(kvc.mixed_workspace_bytes(slots, 0, Hq, Hkv, D), dtype=torch.uint8,
+                      device=dev)
+    out2 = torch.empty_like(out)
+
+    def one_launch(st, dec, pf):
+        n, total = len(st.decode_ids), st.prefill_total_tokens
+        args = {}
+        if n:
+            args.update(q_decode=q[:n], k_new=kv[:n], v_new=kv[:n], decode_block_table=dec[0],
+                        decode_context_lens=dec[1], decode_max_context=st.decode_max_context,
+                        out_decode=out[:n])
+        if total:
+            args.update(q_prefill=q[:total], k_prefill=kv[:total], v_prefill=kv[:total],
+                        cu_chunk_lens=pf[1], prefix_lens=pf[2], prefill_block_table=pf[0],
+                        prefill_max_chunk=st.prefill_max_chunk, out_prefill=out2[:total])
+
+        def run():
+            for c in caches:
+                kvc.mixed_step_attention(c, Hq, softmax_scale=scale, workspace=mws, **args)
+        return run
+
     # 1. the grid
     rows = [1, 2, 4, 8, 16]
     lengths = [8, 16, 24, 32, 48, 64, 96, 128]
@@ -711,24 +732,28 @@ def bench_queue_replay(args):
                  f"continuous batching, {slots} slots, decode first"):
         steps, costs = plans[name]
         k = min(args.direct_steps, len(steps))
-        real = 0.0
+        real = real_one = 0.0
         for st in steps[:k]:
             parts = []
+            dec = pf = None
             if len(st.decode_ids):
                 n = len(st.decode_ids)
-                bt = torch.from_numpy(st.decode_block_table).to(dev)
-                ctx = torch.from_numpy(st.decode_context_lens).to(dev)
-                parts.append(decode_launch(n, bt, ctx, st.decode_max_context))
+                dec = (torch.from_numpy(st.decode_block_table).to(dev),
+                       torch.from_numpy(st.decode_context_lens).to(dev))
+                parts.append(decode_launch(n, dec[0], dec[1], st.decode_max_context))
             if len(st.prefill_ids):
-                bt = torch.from_numpy(st.prefill_block_table).to(dev)
-                cu = torch.from_numpy(st.prefill_cu_chunk_lens).to(dev)
-                pre = torch.from_numpy(st.prefill_prefix_lens).to(dev)
-                parts.append(prefill_launch(st.prefill_total_tokens, cu, pre, bt,
+                pf = (torch.from_numpy(st.prefill_block_table).to(dev),
+                      torch.from_numpy(st.prefill_cu_chunk_lens).to(dev),
+                      torch.from_numpy(st.prefill_prefix_lens).to(dev))
+                parts.append(prefill_launch(st.prefill_total_tokens, pf[1], pf[2], pf[0],
                                             st.prefill_max_chunk))
             real += graph_ms(lambda: [f() for f in parts], 3)
+            real_one += graph_ms(one_launch(st, dec, pf), 3)
         est = float(sum(costs[:k]))
         direct[name] = {"steps": k, "measured_ms": round(real, 3), "estimated_ms": round(est, 3),
-                        "measured_over_estimated": round(real / est, 4)}
+                        "measured_over_estimated": round(real / est, 4),
+                        "measured_one_launch_ms": round(real_one, 3),
+                        "one_launch_speedup": round(real / real_one, 4)}
         print(f"[queue-replay] direct {name}: {k} steps ({time.perf_counter() - t0:.1f} s)",
               file=sys.stderr, flush=True)
 

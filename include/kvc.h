@@ -221,9 +221,11 @@ int kvc_chunked_prefill_attention_split(const kvc_cache* cache, const void* q, c
  * section "The fix that mattered": decode rows plus prefill chunks under a
  * token budget). Computes what kvc_decode_append_attention (decode rows) and
  * kvc_chunked_prefill_attention (chunks) compute, in a persistent kernel whose
- * workgroups take work items from a device queue: first the new K/V writes
- * and a longest-first order of the decode rows, then prefill query tiles and
- * whole decode rows (per kv head) interleaved, each kind largest first.
+ * workgroups take work items from a device queue: first the chunks' K/V
+ * writes (and, for a large decode batch, a longest-first order of the decode
+ * rows), then prefill query tiles (later tiles first), then decode items (one
+ * row and kv head each: the row's new K/V write, then attention over its whole
+ * context).
  * Prefill rows equal kvc_chunked_prefill_attention's bit for bit; decode rows
  * are the same computation with a row's blocks spread over 8 waves of one
  * workgroup instead of split over workgroups (another summation order).

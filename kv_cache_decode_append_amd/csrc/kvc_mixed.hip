@@ -12,24 +12,27 @@
 // slowest workgroup. Here one persistent kernel takes work items from a queue
 // in device memory:
 //
-//   phase 0   item 0 orders the decode rows longest first (by the power of
-//             two of their block count); the next items write the decode
-//             rows' new K/V and the prefill chunks' K/V into the cache, 64
-//             rows each;
+//   phase 0   the prefill chunks' K/V go into the cache, 64 rows per item;
+//             for a large decode batch, one more item first orders the decode
+//             rows longest first (by the power of two of their block count);
 //   then      prefill items, one per (query tile, kv head, chunk), later
 //             query tiles (more keys) first, and decode items, one per (kv
-//             head, row) in that order, each walking the row's whole context,
-//             so no partial results need merging across workgroups. The two
-//             kinds are interleaved in proportion to their counts, so HBM-bound
-//             decode items and MFMA-bound prefill items run side by side on
-//             different compute units, each list largest first.
+//             head, row), each writing the row's new K/V and then walking its
+//             whole context, so no partial results need merging across
+//             workgroups. Prefill items come first (the largest items start
+//             earliest), and the decode items fill in behind them; HBM-bound
+//             decode items and MFMA-bound prefill items then run side by side
+//             on different compute units.
 //
 // Workgroups are 8 waves (the prefill item's shape; a decode item spreads a
-// row's blocks over the 8 waves) and the grid is one resident wave of
-// workgroups. An item after phase 0 waits until every phase-0 item is done
-// (they write what it reads); the wait is bounded and can only be on items
-// that running workgroups already hold. The queue header is reset by the last
-// workgroup to leave.
+// row's blocks over the 8 waves) and the grid is at most one resident wave of
+// workgroups. Workgroup i starts with item i and then takes items from the
+// queue (with a workgroup per item there is no queue, and without phase-0
+// items no atomic at all). A prefill item, and a decode item when the rows are ordered, first
+// waits until every phase-0 item is done (they write what it reads); phase-0
+// items have the lowest indices, so they belong to workgroups dispatched
+// before any that wait, and the wait is bounded anyway. The queue header is
+// reset by the last workgroup to leave.
 
 #include <stdlib.h>
 
@@ -61,17 +64,18 @@ struct MixedArgs {
   const uint8_t* v_pf;
   const uint8_t* k_new; // the decode rows' new K/V, [n_dec][hkv][D]
   const uint8_t* v_new;
-  int32_t n_dec_app;    // phase-0 items for the decode rows' K/V
+  int32_t plan;         // 1: phase-0 item 0 orders the decode rows
   int32_t nc;           // 16-byte chunks per K/V row
   MixedHeader* hdr;
-  int32_t* dec_order;   // [n_dec]: decode rows, longest first
+  int32_t* dec_order;   // [n_dec]: decode rows, longest first (when planned)
   int32_t n_dec;
   int32_t n_pf;
   int32_t n_slices;     // phase-0 items per chunk
-  int32_t n_phase0;     // 1 + n_dec_app + n_pf * n_slices
+  int32_t n_phase0;     // plan + n_pf * n_slices
   int32_t n_pf_items;   // n_qt * hkv * n_pf
   int32_t n_dec_items;  // hkv * n_dec
   int32_t interleave;   // 1: prefill and decode items interleaved, 0: prefill first
+  int32_t one_each;     // the grid has a workgroup per item: no queue
 };
 
 // Item 0 of phase 0: the decode rows in decreasing order of
@@ -105,24 +109,22 @@ __device__ __forceinline__ void plan_decode(const MixedArgs& m, int32_t* scratch
   }
 }
 
-// Phase 0: the new K/V of decode rows [64 * idx, 64 * idx + 64) at position
-// context_len - 1 (rows with an empty context hold no token and are skipped).
-__device__ __forceinline__ void append_decode_rows(const MixedArgs& m, int idx) {
+// The new K/V of decode row b for kv head kvh at position context_len - 1,
+// written by the decode item itself before it reads the row (a workgroup
+// barrier orders the two). A row with an empty context holds no token.
+__device__ __forceinline__ void append_decode_row(const MixedArgs& m, int b, int kvh, int tid) {
   const DecodeArgs& a = m.dec;
-  const int b0 = idx * kAppendRows, b1 = min(m.n_dec, b0 + kAppendRows);
-  const int per_row = a.hkv * m.nc;
-  int bad = 0;
-  for (int i = threadIdx.x; i < (b1 - b0) * per_row; i += kMixThreads) {
-    const int b = b0 + i / per_row, hc = i % per_row;
+  if (tid < m.nc) {
     const int ctx = effective_ctx(a, b, false);
-    if (ctx < 1) continue;
-    // the decode row's new token is row b of k_new: "chunk" of one row at
-    // position ctx - 1
-    bad |= chunk_append_one((uint8_t*)a.kc, (uint8_t*)a.vc, m.k_new, m.v_new,
-                            a.bt + (size_t)b * a.max_blocks, a.max_blocks, a.num_blocks, a.hkv,
-                            m.nc, b, ctx - 1, 0, hc / m.nc, hc % m.nc);
+    if (ctx >= 1) {
+      const int bad = chunk_append_one((uint8_t*)a.kc, (uint8_t*)a.vc, m.k_new, m.v_new,
+                                       a.bt + (size_t)b * a.max_blocks, a.max_blocks,
+                                       a.num_blocks, a.hkv, m.nc, b, ctx - 1, 0, kvh, tid);
+      if (bad && tid == 0) flag_error(a.err, bad);
+    }
   }
-  if (bad) flag_error(a.err, bad);
+  __threadfence_block();
+  __syncthreads();
 }
 
 // Phase 0: rows [64 * slice, 64 * slice + 64) of prefill chunk s.
@@ -164,40 +166,26 @@ __global__ __launch_bounds__(kMixThreads) void mixed_step_kernel(MixedArgs) {
   int32_t* ctl = order_lds + kMixMaxDecode;       // [0] the fetched item
   const int tid = threadIdx.x;
   bool open = false;          // phase 0 seen complete (uniform over the workgroup)
+  bool first = true;
   for (;;) {
     const MixedArgs& m = *fresh_args();
-    if (tid == 0) ctl[0] = atomicAdd(&m.hdr->next, 1);
-    __syncthreads();
-    const int item = ctl[0];
+    int item = blockIdx.x;
+    if (!first) {
+      if (m.one_each) break;
+      if (tid == 0) ctl[0] = (int)gridDim.x + atomicAdd(&m.hdr->next, 1);
+      __syncthreads();
+      item = ctl[0];
+    }
+    first = false;
     if (item < m.n_phase0) {
-      if (item == 0)
+      if (m.plan && item == 0)
         plan_decode(m, reinterpret_cast<int32_t*>(smem));
-      else if (item <= m.n_dec_app)
-        append_decode_rows(m, item - 1);
       else
-        append_slice(m, item - 1 - m.n_dec_app);
+        append_slice(m, item - m.plan);
       __threadfence();                             // publish this item's writes
       __syncthreads();
       if (tid == 0) atomicAdd(&m.hdr->phase0_done, 1);
     } else {
-      if (!open) {
-        if (tid == 0) {
-          int spins = 0;
-          while (__hip_atomic_load(&m.hdr->phase0_done, __ATOMIC_ACQUIRE,
-                                   __HIP_MEMORY_SCOPE_AGENT) < m.n_phase0) {
-            __builtin_amdgcn_s_sleep(4);
-            if (++spins == kSpinLimit) {
-              flag_error(m.dec.err, KVC_DEVERR_QUEUE);
-              break;
-            }
-          }
-        }
-        __syncthreads();
-        __threadfence();                           // see every phase-0 write
-        for (int i = tid; i < m.n_dec; i += kMixThreads) order_lds[i] = m.dec_order[i];
-        __syncthreads();
-        open = true;
-      }
       // item -> (prefill or decode, index in that list)
       const int k = item - m.n_phase0;
       const int64_t n_pf = m.n_pf_items, n_all = n_pf + m.n_dec_items;
@@ -212,6 +200,25 @@ __global__ __launch_bounds__(kMixThreads) void mixed_step_kernel(MixedArgs) {
         is_pf = k < n_pf;
         idx = is_pf ? k : k - (int)n_pf;
       }
+      if (!open && (is_pf || m.plan)) {
+        if (tid == 0) {
+          int spins = 0;
+          while (__hip_atomic_load(&m.hdr->phase0_done, __ATOMIC_ACQUIRE,
+                                   __HIP_MEMORY_SCOPE_AGENT) < m.n_phase0) {
+            __builtin_amdgcn_s_sleep(4);
+            if (++spins == kSpinLimit) {
+              flag_error(m.dec.err, KVC_DEVERR_QUEUE);
+              break;
+            }
+          }
+        }
+        __syncthreads();
+        __threadfence();                           // see every phase-0 write
+        if (m.plan)
+          for (int i = tid; i < m.n_dec; i += kMixThreads) order_lds[i] = m.dec_order[i];
+        __syncthreads();
+        open = true;
+      }
       const int hkv = m.dec.hkv;
       // the thread index, opaque here too, so that nothing derived from it is
       // hoisted out of the loop and held in vector registers across items
@@ -225,15 +232,15 @@ __global__ __launch_bounds__(kMixThreads) void mixed_step_kernel(MixedArgs) {
         prefill_item<T, D, G>(mi.pf, qt + mi.pf.n_qt * (kvh + hkv * s), smem, my_tid);
       } else {
         const MixedArgs& mi = *fresh_args();
-        decode_item<T, D, G, kMixWaves, true, false>(mi.dec, idx % hkv, order_lds[idx / hkv], 0,
-                                                     smem, my_tid);
+        const int b = mi.plan ? order_lds[idx / hkv] : idx / hkv, kvh = idx % hkv;
+        append_decode_row(mi, b, kvh, my_tid);
+        decode_item<T, D, G, kMixWaves, true, false>(mi.dec, kvh, b, 0, smem, my_tid);
       }
     }
     __syncthreads();                               // LDS and ctl free for the next item
   }
-  if (tid == 0) {
-    const MixedArgs& m = *fresh_args();
-    __threadfence();
+  const MixedArgs& m = *fresh_args();
+  if (tid == 0 && (!m.one_each || m.n_phase0 > 0)) {
     if (atomicAdd(&m.hdr->exited, 1) == (int)gridDim.x - 1) {
       atomicExch(&m.hdr->next, 0);
       atomicExch(&m.hdr->phase0_done, 0);
@@ -249,12 +256,15 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // Workspace: the 256-byte queue header, then the decode row order.
 size_t mixed_ws_bytes(int n_dec) { return 256 + align256((size_t)n_dec * 4); }
 
-// Prefill and decode items interleaved (default) or prefill first
-// (KVC_MIXED_ORDER=0).
+// Prefill items first, then decode items (default), or the two interleaved in
+// proportion to their counts (KVC_MIXED_ORDER=1). On the skewed 210-sequence
+// step prefill first is faster (2.65 against 2.76 ms per layer): the largest
+// items (late query tiles over long prefixes) start earliest and the short
+// decode items fill the tail.
 int mixed_interleave() {
   static const int v = [] {
     const char* e = getenv("KVC_MIXED_ORDER");
-    return e && atoi(e) == 0 ? 0 : 1;
+    return e && atoi(e) == 1 ? 1 : 0;
   }();
   return v;
 }
@@ -276,8 +286,10 @@ int launch_mixed(const MixedArgs& m, int64_t n_items_max, hipStream_t st) {
     cached[dev][1] = per_cu;
   }
   const int64_t grid = std::min<int64_t>(n_items_max, (int64_t)cached[dev][0] * cached[dev][1]);
+  MixedArgs mm = m;
+  mm.one_each = grid == n_items_max ? 1 : 0;
   hipLaunchKernelGGL((mixed_step_kernel<T, D, G>), dim3((unsigned)grid), dim3(kMixThreads), 0, st,
-                     m);
+                     mm);
   return launch_status();
 }
 
@@ -401,14 +413,16 @@ extern "C" int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_
   m.v_pf = reinterpret_cast<const uint8_t*>(b.v_prefill);
   m.k_new = reinterpret_cast<const uint8_t*>(b.k_new);
   m.v_new = reinterpret_cast<const uint8_t*>(b.v_new);
-  m.n_dec_app = (int)ceil_div(n_dec, kAppendRows);
+  // order the decode rows only when there are many more decode items than
+  // workgroups and some row is long enough for its order to matter
+  m.plan = (int64_t)n_dec * hkv > 2 * 256 && b.decode_max_context > 4096 ? 1 : 0;
   m.nc = D * dtype_bytes(cache->dtype) / 16;
   m.hdr = reinterpret_cast<MixedHeader*>(ws);
   m.dec_order = reinterpret_cast<int32_t*>(ws + 256);
   m.n_dec = n_dec;
   m.n_pf = has_pf ? b.n_prefill : 0;
   m.n_slices = has_pf ? (int)ceil_div(b.prefill_max_chunk, kAppendRows) : 0;
-  const int64_t n_phase0 = 1 + m.n_dec_app + (int64_t)m.n_pf * m.n_slices;
+  const int64_t n_phase0 = m.plan + (int64_t)m.n_pf * m.n_slices;
   const int64_t n_items_max = n_phase0 + p.n_work + (int64_t)n_dec * hkv;
   if (n_items_max > INT32_MAX / 2) return KVC_ERR_SHAPE;
   m.n_phase0 = (int)n_phase0;
