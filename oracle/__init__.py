@@ -16,6 +16,8 @@ Everything here is plain, slow and meant to be read against the pages:
 * ``sizes``: KV bytes per token and the capacity arithmetic.
 * ``prefix``: prefix caching, i.e. whole-block matching of a prompt's opening
   tokens against cached blocks, with reference counts and block reuse.
+* ``quant``: fp8 (E4M3) quantisation of KV rows with one scale per token and
+  kv head.
 * ``sched``: iteration-level scheduling of a request queue (continuous
   batching under decode-first or prefill-first steps, static batching).
 
@@ -23,4 +25,4 @@ Every function is pinned by a CPU test (``tests/test_oracle_*.py``) against
 values the pages print, closed forms, special cases, library routines or
 brute force; see each function's docstring for its pin.
 """
-from . import attention, bf16, paged, prefix, sched, sizes  # noqa: F401
+from . import attention, bf16, paged, prefix, quant, sched, sizes  # noqa: F401
