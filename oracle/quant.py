@@ -15,7 +15,8 @@ in the design doc), the plainest ones that keep every value of a row recoverable:
   scale = amax / 448 with amax = max |x| over the row; the stored codes are
   the values x * (448 / amax) rounded to the nearest E4M3 value, ties to the
   even code, magnitudes above 448 (reachable only by rounding) clamped to 448;
-  a row of zeros gets scale 0 and zero codes;
+  a row whose amax is below 2^-100 (zeros, or values so small that 448 / amax
+  would not stay finite in fp32) gets scale 0 and zero codes;
 * both products and the quotients are single fp32 operations rounded to
   nearest even, in this order: inv = fl(448 / amax), y = fl(x * inv),
   scale = fl(amax / 448);
@@ -32,6 +33,7 @@ from __future__ import annotations
 import numpy as np
 
 E4M3_MAX = 448.0
+ZERO_ROW_AMAX = 2.0 ** -100    # rows with a smaller amax are stored as zeros
 
 
 def e4m3_value(code: int) -> float:
@@ -77,7 +79,7 @@ def quantize_rows(x):
     the rows x[..., :] (float32 values; the last axis is head_dim)."""
     x = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(x), axis=-1)
-    zero = amax == 0
+    zero = amax < np.float32(ZERO_ROW_AMAX)
     safe = np.where(zero, np.float32(1.0), amax).astype(np.float32)
     inv = (np.float32(E4M3_MAX) / safe).astype(np.float32)
     y = (x * inv[..., None]).astype(np.float32)

@@ -53,11 +53,16 @@ def pin_rows(q=Q):
     rng = np.random.default_rng(9)
     x = (rng.standard_normal((40, 8, 128)) * rng.uniform(0.01, 30, (40, 8, 1))).astype(np.float32)
     x[3, 2] = 0.0
+    x[4, 1] = np.float32(2.0 ** -101)              # below the zero-row limit
+    x[4, 2, :3] = np.float32(2.0 ** -99)           # above it: an ordinary row
+    x[4, 2, 3:] = 0.0
     codes, scales = q.quantize_rows(x)
     assert codes.shape == x.shape and scales.shape == x.shape[:2] and scales.dtype == np.float32
     assert scales[3, 2] == 0 and not codes[3, 2].any()
+    assert scales[4, 1] == 0 and not codes[4, 1].any()
+    assert np.all(codes[4, 2, :3] == 0x7E) and scales[4, 2] == np.float32(2.0 ** -99) / np.float32(448)
     amax = np.abs(x).max(-1)
-    nz = amax > 0
+    nz = amax >= 2.0 ** -100
     # the row's largest magnitude maps to +-448, the scale is amax / 448 in fp32
     assert np.all((codes & 0x7F).max(-1)[nz] == 0x7E)
     assert np.array_equal(scales[nz], (amax / np.float32(448)).astype(np.float32)[nz])
@@ -68,12 +73,13 @@ def pin_rows(q=Q):
     s = scales.astype(np.float64)[..., None]
     bound = np.maximum(np.abs(x) * 2.0 ** -4, s * 2.0 ** -10) * (1 + 2.0 ** -20) + \
         np.abs(x) * 2.0 ** -22
-    assert np.all(err <= bound)
+    assert np.all(err[nz] <= bound[nz])
+    assert np.all(err[~nz] < 2.0 ** -100)           # rows stored as zeros
     # a row and its sign flip, a row times a power of two: same codes up to sign / same codes
     c2, s2 = q.quantize_rows(-x)
     assert np.array_equal(c2[nz] & 0x7F, codes[nz] & 0x7F) and np.array_equal(s2, scales)
     c3, s3 = q.quantize_rows(x * np.float32(4))
-    assert np.array_equal(c3, codes) and np.array_equal(s3, scales * np.float32(4))
+    assert np.array_equal(c3[nz], codes[nz]) and np.array_equal(s3[nz], scales[nz] * np.float32(4))
 
 
 PINS = [pin_values, pin_encoding, pin_rows]
