@@ -47,8 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--workload", default="c3-decode",
-                    choices=["c3-decode", "c4-mixed", "c5-decode", "c5-prefill", "prefix-warm",
-                             "queue-replay"])
+                    choices=["c3-decode", "c3-fp8", "c4-mixed", "c5-decode", "c5-prefill",
+                             "prefix-warm", "queue-replay"])
     ap.add_argument("--direct-steps", type=int, default=400,
                     help="queue-replay: leading steps of each continuous plan run for real")
     return ap.parse_args()
@@ -154,6 +154,8 @@ def main():
         return bench_c4_mixed(args)
     if args.workload == "queue-replay":
         return bench_queue_replay(args)
+    if args.workload == "c3-fp8":
+        return bench_c3_fp8(args)
 
     import torch
 
@@ -270,6 +272,84 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_budget_s)
+    print(json.dumps(res), flush=True)
+
+
+def bench_c3_fp8(args):
+    """The C3 decode step over an fp8 (E4M3, one fp32 scale per token and kv
+    head) cache: same batch, contexts, pools and launch pattern as the default
+    workload, K/V codes and scales instead of bf16 values. KV bytes per token
+    and kv head: 2 x (head_dim + 4). Queries, new K/V and outputs stay bf16."""
+    import torch
+
+    import kv_cache_decode_append_amd as kvc
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.C3
+    L = args.layers
+    ctx_np = W.context_lengths(w)
+    bt_np = W.block_tables(w, ctx_np, W.C3_POOL_BLOCKS)
+    B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
+    nb = W.C3_POOL_BLOCKS
+    max_ctx = int(ctx_np.max())
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    caches = []
+    for layer in range(L):
+        c = kvc.PagedKVCache.allocate(nb, Hkv, D, torch.float8_e4m3fn, device=dev)
+        for pool in (c.k_cache, c.v_cache):
+            # finite codes: magnitude field 0x00..0x7E, either sign
+            code = torch.randint(0, 0x7F, pool.shape, generator=g, device=dev, dtype=torch.int32)
+            sign = torch.randint(0, 2, pool.shape, generator=g, device=dev, dtype=torch.int32)
+            pool.view(torch.uint8).copy_((code | (sign << 7)).to(torch.uint8))
+        c.k_scale.uniform_(0.5 / 448, 2.0 / 448, generator=g)
+        c.v_scale.uniform_(0.5 / 448, 2.0 / 448, generator=g)
+        caches.append(c)
+    q = [torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5, generator=g)
+         for _ in range(L)]
+    kn = [torch.empty(B, Hkv, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5, generator=g)
+          for _ in range(L)]
+    vn = [torch.empty(B, Hkv, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5, generator=g)
+          for _ in range(L)]
+    out = [torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    bt = torch.from_numpy(bt_np).to(dev)
+    ctx = torch.from_numpy(ctx_np.astype(np.int32)).to(dev)
+    ws = torch.empty(max(1, kvc.decode_workspace_bytes(B, Hq, D, max_ctx)), dtype=torch.uint8,
+                     device=dev)
+
+    def step(i):
+        for layer in range(L):
+            kvc.decode_append_attention(caches[layer], q[layer], kn[layer], vn[layer], bt, ctx,
+                                        max_ctx, out=out[layer], workspace=ws)
+
+    ms_per_step = _timed(step, args.steps, args.warmup)
+    errs = [int(c.err_flag.item()) for c in caches]
+    if any(errs) or not all(torch.isfinite(o.float()).all().item() for o in out):
+        print(f"bench sanity check failed: err flags {errs}", file=sys.stderr)
+        sys.exit(1)
+    kv_bytes_layer = int(ctx_np.sum()) * Hkv * (D + 4) * 2
+    io_bytes_layer = (B * Hq * D * 2 * 2 + B * Hkv * D * 2 * 2 + B * Hkv * (D + 4) * 2
+                      + B * bt_np.shape[1] * 4 + B * 4)
+    kv_gbs = kv_bytes_layer * L / (ms_per_step * 1e-3) / 1e9
+    avg_us = ms_per_step * 1e3 / L
+    achieved = (kv_bytes_layer + io_bytes_layer) / (avg_us * 1e-6) / 1e9
+    res = _base_line(args, "decode-attn KV-read GB/s + batched decode steps/s, B=64 ctx~2k, fp8 "
+                     "E4M3 cache (per-row scales)", round(kv_gbs, 1), "GB/s", ms_per_step,
+                     "fp8-e4m3 cache, bf16 compute",
+                     {"workload": "llama3.1-8b attention decode, B=64, ctx U[2000,2300], GQA 32/8, "
+                                  "head_dim 128, fp8 E4M3 paged cache with one fp32 scale per "
+                                  "token and kv head, 32 layers",
+                      "B": B, "layers": L, "ctx_sum": int(ctx_np.sum()),
+                      "kv_bytes_per_layer": kv_bytes_layer},
+                     {"bound": "hbm", "kernel": "paged_decode_kernel<fp8> (fused quantising "
+                      "append + decode attention, one launch per layer)",
+                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                      "avg_us": round(avg_us, 2), "bytes_per_launch": kv_bytes_layer + io_bytes_layer})
+    res["pct_hbm_peak"] = round(100.0 * kv_gbs / HBM_PEAK_GBS, 2)
+    res["decode_steps_per_s"] = round(1000.0 / ms_per_step, 2)
     print(json.dumps(res), flush=True)
 
 

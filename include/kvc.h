@@ -42,6 +42,19 @@
  *     so one (block, kv-head) tile is contiguous (4 KiB for head_dim 128, bf16).
  *   - Supported: dtype fp32 (head_dim 16, 32, 64, 128) and bf16 (head_dim 32,
  *     64, 128); G = Hq / Hkv in {1, 2, 4, 8}; block_size 16.
+ *   - Quantised cache (KVC_FP8): the pools hold OCP FP8 E4M3 codes and two
+ *     more fp32 pools hold one scale per (block, kv head, token) row, laid out
+ *     [num_blocks][num_kv_heads][16]. A row x of head_dim values is stored as
+ *     scale = amax / 448 (amax = max |x|) and codes = E4M3(x * (448 / amax))
+ *     rounded to nearest, ties to even, clamped at 448 (a row with amax below
+ *     2^-100: scale 0, codes 0); its value is code * scale. The gouthm.com page ("The KV cache
+ *     is not your bottleneck", sections "The setup" and "What the profile
+ *     said") names quantising the cache for memory headroom at a small
+ *     accuracy cost and gives no scheme; this one keeps each appended row
+ *     independent of the rows after it. Queries, new K/V and outputs are bf16.
+ *     Supported by kvc_kv_append, kvc_paged_decode_attention and
+ *     kvc_decode_append_attention with head_dim 64 or 128; the prefill and
+ *     mixed-step calls return KVC_ERR_UNSUPPORTED for such a cache.
  */
 #ifndef KVC_H
 #define KVC_H
@@ -53,7 +66,7 @@
 extern "C" {
 #endif
 
-typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1, KVC_FP8 = 2 } kvc_dtype;
 
 enum {
   KVC_OK = 0,
@@ -88,6 +101,8 @@ typedef struct {
   int32_t head_dim;
   int32_t dtype;      /* kvc_dtype */
   int32_t* err_flag;  /* optional device int32 (may be NULL), see KVC_DEVERR_* */
+  float* k_scale;     /* KVC_FP8 only: [num_blocks][num_kv_heads][16] fp32 row scales */
+  float* v_scale;     /* (NULL for the other dtypes) */
 } kvc_cache;
 
 /* Host-only. Raw K+V bytes one token occupies across `layers` layers:
@@ -115,7 +130,9 @@ int kvc_slot_mapping(const int32_t* block_table, int32_t n_seqs, int32_t max_blo
 
 /* Append: k_cache[slot / bs][h][slot % bs][:] = k[t][h][:], same for v.
  *   k, v          device [T][num_kv_heads][head_dim], cache dtype (no conversion:
- *                 the cache contents are bit-exact copies)
+ *                 the cache contents are bit-exact copies); bf16 for a KVC_FP8
+ *                 cache, whose rows are quantised as the header describes
+ *                 (codes into the pools, scales into k_scale / v_scale)
  *   slot_mapping  device int64 [T]; slot < 0 skips the token
  * T may be 0 (nothing is launched). */
 int kvc_kv_append(const kvc_cache* cache, const int64_t* slot_mapping, const void* k,
@@ -127,15 +144,16 @@ size_t kvc_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim,
                                   int32_t max_context_len);
 
 /* Paged GQA decode attention for a batch of sequences of mixed lengths.
- *   q             device [B][Hq][head_dim], cache dtype: each sequence's newest query
+ *   q             device [B][Hq][head_dim], cache dtype (bf16 for KVC_FP8): each
+ *                 sequence's newest query
  *   block_table   device int32 [B][max_blocks]
  *   context_lens  device int32 [B]: tokens in each sequence's cache INCLUDING the
  *                 newest one (append first, then attend). 0 gives a zero output.
  *   max_context_len  host-known upper bound of context_lens (sizes the grid;
  *                 no device-to-host copy is made)
  *   softmax_scale usually 1/sqrt(head_dim)
- *   out           device [B][Hq][head_dim], cache dtype (bf16 outputs are rounded
- *                 to nearest even)
+ *   out           device [B][Hq][head_dim], cache dtype (bf16 for KVC_FP8; bf16
+ *                 outputs are rounded to nearest even)
  *   workspace     device scratch of >= kvc_decode_workspace_bytes(...) bytes, no
  *                 initialisation needed; may be NULL when max_context_len fits one
  *                 partition (the size query then returns 0).
@@ -148,8 +166,9 @@ int kvc_paged_decode_attention(const kvc_cache* cache, const void* q, int32_t B,
                                size_t workspace_bytes, void* stream);
 
 /* One decode step in one launch: for every sequence b with context_lens[b] >= 1,
- * write k_new[b], v_new[b] ([num_kv_heads][head_dim], cache dtype) at position
- * context_lens[b] - 1 through the block table (append first), then attend q[b]
+ * write k_new[b], v_new[b] ([num_kv_heads][head_dim], cache dtype; bf16 for
+ * KVC_FP8, quantised on write) at position context_lens[b] - 1 through the
+ * block table (append first), then attend q[b]
  * over positions 0 .. context_lens[b] - 1 (aiwithghost.com, section "What does a
  * KV cache keep?": compute the new token's K/V/Q, append, attend over everything
  * stored). Same arguments, outputs and workspace rule as

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     DEVERR_SLOT,
     KVC_BF16,
     KVC_F32,
+    KVC_FP8,
     LIB,
     LIB_PATH,
     KvcError,

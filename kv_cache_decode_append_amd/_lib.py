@@ -18,11 +18,11 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvc.so")
 
-KVC_F32, KVC_BF16 = 0, 1
+KVC_F32, KVC_BF16, KVC_FP8 = 0, 1, 2
 DEVERR_BLOCK_ID, DEVERR_SLOT, DEVERR_CONTEXT, DEVERR_QUEUE = 1, 2, 4, 8
 BLOCK_SIZE = 16
 
-_DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
+_DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16, torch.float8_e4m3fn: KVC_FP8}
 
 
 class KvcError(RuntimeError):
@@ -41,6 +41,8 @@ class _CCache(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("err_flag", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -172,27 +174,40 @@ class PagedKVCache:
     """One layer's K and V block pools, [num_blocks, Hkv, 16, head_dim] each.
 
     The tensors are owned by the caller (allocated here with torch for
-    convenience); the library only reads and writes them.
+    convenience); the library only reads and writes them. A float8_e4m3fn
+    cache also has K and V row scales, [num_blocks, Hkv, 16] float32 each;
+    its queries, new K/V and outputs are bfloat16 (``dtype``).
     """
 
     def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                 err_flag: torch.Tensor | None = None):
+                 err_flag: torch.Tensor | None = None, k_scale: torch.Tensor | None = None,
+                 v_scale: torch.Tensor | None = None):
         _need(k_cache, "k_cache", ndim=4)
         _need(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4, device=k_cache.device)
         if k_cache.shape != v_cache.shape:
             raise ValueError("k_cache and v_cache shapes differ")
         if k_cache.dtype not in _DTYPE_CODE:
-            raise TypeError(f"cache dtype {k_cache.dtype} is not fp32 or bf16")
+            raise TypeError(f"cache dtype {k_cache.dtype} is not fp32, bf16 or float8_e4m3fn")
         if k_cache.shape[2] != BLOCK_SIZE:
             raise ValueError("block size must be 16")
         if err_flag is not None:
             _need(err_flag, "err_flag", dtype=torch.int32, device=k_cache.device)
-        self.k_cache, self.v_cache, self.err_flag = k_cache, v_cache, err_flag
         nb, hkv, _, d = k_cache.shape
+        fp8 = k_cache.dtype == torch.float8_e4m3fn
+        if fp8:
+            for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+                _need(t, n, torch.float32, 3, k_cache.device)
+                if t.shape != (nb, hkv, BLOCK_SIZE):
+                    raise ValueError(f"{n} must be [{nb}, {hkv}, {BLOCK_SIZE}]")
+        elif k_scale is not None or v_scale is not None:
+            raise ValueError("row scales belong to a float8_e4m3fn cache only")
+        self.k_cache, self.v_cache, self.err_flag = k_cache, v_cache, err_flag
+        self.k_scale, self.v_scale = k_scale, v_scale
         self.num_blocks, self.num_kv_heads, self.head_dim = nb, hkv, d
-        self.dtype = k_cache.dtype
+        self.storage_dtype = k_cache.dtype
+        self.dtype = torch.bfloat16 if fp8 else k_cache.dtype
         self._c = _CCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, BLOCK_SIZE, hkv, d,
-                          _DTYPE_CODE[k_cache.dtype], _ptr(err_flag))
+                          _DTYPE_CODE[k_cache.dtype], _ptr(err_flag), _ptr(k_scale), _ptr(v_scale))
 
     @classmethod
     def allocate(cls, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
@@ -200,12 +215,19 @@ class PagedKVCache:
         shape = (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim)
         k = torch.empty(shape, dtype=dtype, device=device)
         v = torch.empty(shape, dtype=dtype, device=device)
+        ks = vs = None
+        if dtype == torch.float8_e4m3fn:
+            ks = torch.empty(shape[:3], dtype=torch.float32, device=device)
+            vs = torch.empty(shape[:3], dtype=torch.float32, device=device)
         if fill_bits is not None:
-            ib = torch.int16 if dtype == torch.bfloat16 else torch.int32
+            ib = {torch.bfloat16: torch.int16, torch.float8_e4m3fn: torch.int8}.get(dtype, torch.int32)
             k.view(ib).fill_(fill_bits)
             v.view(ib).fill_(fill_bits)
+            if ks is not None:
+                ks.view(torch.int32).fill_(fill_bits)
+                vs.view(torch.int32).fill_(fill_bits)
         err = torch.zeros(1, dtype=torch.int32, device=device) if with_err_flag else None
-        return cls(k, v, err)
+        return cls(k, v, err, ks, vs)
 
     @property
     def c(self):

@@ -70,6 +70,47 @@ __global__ void kv_append_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__
   *reinterpret_cast<u32x4*>(vc + dst) = *reinterpret_cast<const u32x4*>(v + src);
 }
 
+// fp8 cache: one 8-value chunk of a (token, kv head) row per thread. The NCB =
+// head_dim / 8 threads of a row (an aligned group of 8 or 16 lanes) find the
+// row's largest magnitude together, then each codes its 8 values with the
+// row's scale (amax / 448; a row below kZeroRowAmax is stored as zeros) and
+// the first stores the scale.
+template <int NCB>
+__global__ __launch_bounds__(256) void kv_append_fp8_kernel(
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ ks,
+    float* __restrict__ vs, const int64_t* __restrict__ slots, const uint8_t* __restrict__ k,
+    const uint8_t* __restrict__ v, int64_t n_chunks, int32_t hkv, int64_t num_slots,
+    int32_t* err) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool in = i < n_chunks;
+  const int64_t row = i / NCB;            // (t, h)
+  const int32_t c = (int32_t)(i % NCB);
+  const int64_t t = row / hkv;
+  const int32_t h = (int32_t)(row - t * hkv);
+  const int64_t slot = in ? slots[t] : -1;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const u32x4 kx = in ? *reinterpret_cast<const u32x4*>(k + i * 16) : zero;
+  const u32x4 vx = in ? *reinterpret_cast<const u32x4*>(v + i * 16) : zero;
+  // every lane of the group takes part in the reductions, so no early exit above
+  const float ka = group_max<NCB>(bf16x8_amax(kx));
+  const float va = group_max<NCB>(bf16x8_amax(vx));
+  if (!in || slot < 0) return;
+  if (slot >= num_slots) {
+    if (h == 0 && c == 0) flag_error(err, KVC_DEVERR_SLOT);
+    return;
+  }
+  const int64_t prow = ((slot >> 4) * hkv + h) * 16 + (slot & 15);   // row of the pools
+  const bool kz = !(ka >= kZeroRowAmax), vz = !(va >= kZeroRowAmax);
+  const u32x2 kq = kz ? u32x2{0u, 0u} : bf16x8_to_e4m3x8(kx, kE4M3Max / ka);
+  const u32x2 vq = vz ? u32x2{0u, 0u} : bf16x8_to_e4m3x8(vx, kE4M3Max / va);
+  *reinterpret_cast<u32x2*>(kc + prow * (NCB * 8) + c * 8) = kq;
+  *reinterpret_cast<u32x2*>(vc + prow * (NCB * 8) + c * 8) = vq;
+  if (c == 0) {
+    ks[prow] = kz ? 0.f : ka / kE4M3Max;
+    vs[prow] = vz ? 0.f : va / kE4M3Max;
+  }
+}
+
 // Prefill-chunk write: token r of sequence s (r < C_s) goes to position
 // prefix_s + r. grid = (ceil(max_chunk * hkv * nc / 256), n_seqs).
 __global__ void chunk_append_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
@@ -132,6 +173,17 @@ extern "C" int kvc_kv_append(const kvc_cache* cache, const int64_t* slot_mapping
   if (T < 0) return KVC_ERR_SHAPE;
   if (T == 0) return KVC_OK;
   if (!slot_mapping || !k || !v) return KVC_ERR_NULL;
+  if (cache->dtype == KVC_FP8) {
+    const int ncb = cache->head_dim / 8;
+    const int64_t n = (int64_t)T * cache->num_kv_heads * ncb;
+    auto kern = ncb == 16 ? kvc::kv_append_fp8_kernel<16> : kvc::kv_append_fp8_kernel<8>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)kvc::ceil_div(n, 256)), dim3(256), 0,
+                       kvc::as_stream(stream), (uint8_t*)cache->k_cache, (uint8_t*)cache->v_cache,
+                       cache->k_scale, cache->v_scale, slot_mapping, (const uint8_t*)k,
+                       (const uint8_t*)v, n, cache->num_kv_heads,
+                       (int64_t)cache->num_blocks * 16, cache->err_flag);
+    return kvc::launch_status();
+  }
   const int nc = cache->head_dim * kvc::dtype_bytes(cache->dtype) / 16;
   const int64_t n_chunks = (int64_t)T * cache->num_kv_heads * nc;
   hipLaunchKernelGGL(kvc::kv_append_kernel, dim3((unsigned)kvc::ceil_div(n_chunks, 256)), dim3(256),

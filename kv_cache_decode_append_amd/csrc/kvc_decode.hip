@@ -12,7 +12,7 @@ constexpr int kMaxPartBlocks = kWaves * 64;   // one block id per lane of each w
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeShape<T, D, G, kWaves>::SMEM];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeShape<ComputeT<T>, D, G, kWaves>::SMEM];
   // One-dimensional grid, kv head fastest, then sequence, partition slowest:
   // workgroups are dealt round-robin to the 8 XCDs by linear index, so every
   // partition level spreads over all of them. (With the partition fastest, a
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int32_t 
     float A = 0.f;
     for (int i = 0; i < n_used; ++i)
       A += __builtin_amdgcn_exp2f(ml[i].x - M) * a.ws_o[((size_t)row * a.n_part + i) * D + d];
-    store_out<T>(a.out, (size_t)row * D + d, A * inv);
+    store_out<ComputeT<T>>(a.out, (size_t)row * D + d, A * inv);
   }
 }
 
@@ -78,11 +78,16 @@ int dispatch_decode(const DecodeArgs& a, int dtype, int D, int B, int G, hipStre
       case 64: return dispatch_g<float, 64>(a, B, G, st);
       case 128: return dispatch_g<float, 128>(a, B, G, st);
     }
-  } else {
+  } else if (dtype == KVC_BF16) {
     switch (D) {
       case 32: return dispatch_g<bf16_tag, 32>(a, B, G, st);
       case 64: return dispatch_g<bf16_tag, 64>(a, B, G, st);
       case 128: return dispatch_g<bf16_tag, 128>(a, B, G, st);
+    }
+  } else {
+    switch (D) {
+      case 64: return dispatch_g<fp8_tag, 64>(a, B, G, st);
+      case 128: return dispatch_g<fp8_tag, 128>(a, B, G, st);
     }
   }
   return KVC_ERR_UNSUPPORTED;
@@ -169,6 +174,8 @@ static int decode_entry(const kvc_cache* cache, const void* q, const void* k_new
   a.part_blocks = pb;
   a.n_part = n_part;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.ks = cache->k_scale;
+  a.vs = cache->v_scale;
   return dispatch_decode(a, cache->dtype, cache->head_dim, B, G, as_stream(stream));
 }
 

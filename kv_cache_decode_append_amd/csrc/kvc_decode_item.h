@@ -78,6 +78,11 @@ struct DecodeShape {
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "G in {1,2,4,8}");
 };
 
+// Type the kernels compute in: fp8 codes are converted to bf16 (exactly) and
+// then take the bf16 path.
+template <typename T>
+using ComputeT = std::conditional_t<std::is_same_v<T, fp8_tag>, bf16_tag, T>;
+
 struct DecodeArgs {
   const void* q;
   const void* k_new;  // fused append: [B][hkv][D] new K/V at position ctx-1, or null
@@ -98,6 +103,8 @@ struct DecodeArgs {
   int32_t part_blocks;
   int32_t n_part;
   float scale_log2;   // softmax scale * log2(e)
+  float* ks;          // fp8 caches: row scales [num_blocks][hkv][16] of K and V
+  float* vs;
 };
 
 // Context length the kernels use: clamped to what the grid and table cover.
@@ -169,7 +176,14 @@ __device__ __forceinline__ void unpack<float, 4>(const u32x4& v, float (&x)[4]) 
 template <typename T, int D, int G, int NW, bool WHOLE = false, bool FUSE = true>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b, int part,
                                             uint8_t* smem, int tid = threadIdx.x) {
-  using S = DecodeShape<T, D, G, NW>;
+  using C = ComputeT<T>;
+  using S = DecodeShape<C, D, G, NW>;
+  constexpr bool F8 = std::is_same_v<T, fp8_tag>;
+  constexpr int TILE_MEM = F8 ? 16 * D : S::TILE;   // bytes of one (block, kv head) tile
+  // fp8 blocks in flight per wave (half a bf16 block each). Three fit in 256
+  // registers at head_dim 128 with G <= 4, but on the C3 step two are faster
+  // (514 against 491 steps/s): the wave is not waiting on memory there.
+  constexpr int PF = F8 ? (D == 128 && G >= 4 ? 2 : 3) : S::PF;
   const int lane = tid & 63;
   // the wave index is uniform across the wave; saying so keeps every buffer
   // descriptor and loop bound in scalar registers (no per-lane waterfall)
@@ -182,7 +196,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
   if (part >= n_used) return;
   if (ctx == 0) {
     for (int o = tid; o < G * D; o += NW * 64)
-      store_out<T>(a.out, ((size_t)b * hq_all + kvh * G) * D + o, 0.f);
+      store_out<C>(a.out, ((size_t)b * hq_all + kvh * G) * D + o, 0.f);
     return;
   }
   const int blk_end = min(part * a.part_blocks + a.part_blocks, nblk);
@@ -223,7 +237,22 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     n_my = (end - blk0 > w) ? (end - blk0 - w + NW - 1) / NW : 0;
     my_blk = lane < n_my ? bt_row[blk0 + w + lane * NW] : -1;
   };
+  // the first range's block ids are loaded here, next to the query, so that
+  // the loads of the new row below are not behind them in the load counter
+  start_range();
 
+  // fp8: tile index (block id * Hkv + kv head) of this wave's i-th block, or -1.
+  auto tile_of = [&](int i) -> int64_t {
+    int64_t tile = -1;
+    if (i < n_my) {
+      const int blk = __builtin_amdgcn_readlane(my_blk, i);
+      if ((unsigned)blk < (unsigned)a.num_blocks)
+        tile = (int64_t)blk * a.hkv + kvh;
+      else if (lane == 0)
+        flag_error(a.err, KVC_DEVERR_BLOCK_ID);
+    }
+    return tile;
+  };
   // Issue the loads of this wave's i-th block into (kb, vb).
   auto issue = [&](u32x4 (&kb)[S::NI], u32x4 (&vb)[S::NI], int i) {
     size_t off = 0;
@@ -244,6 +273,29 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
 #pragma unroll
     for (int j = 0; j < S::NI; ++j) vb[j] = buffer_load16_stream(rv, (uint32_t)(j * 64 + lane) * 16u);
   };
+  // fp8: the codes of the same (token, 8 values) each bf16 load would hold,
+  // 8 bytes per lane, and the tile's row scales (lane l: token l % 16).
+  auto issue8 = [&](u32x2 (&kr)[S::NI], u32x2 (&vr)[S::NI], float& sk, float& sv, int i) {
+    const int64_t tile = tile_of(i);
+    const size_t off = tile >= 0 ? (size_t)tile * TILE_MEM : 0;
+    const uint32_t bytes = tile >= 0 ? TILE_MEM : 0;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + off, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + off, bytes);
+    const __amdgpu_buffer_rsrc_t rks = make_rsrc(a.ks + (tile >= 0 ? tile * 16 : 0), tile >= 0 ? 64u : 0u);
+    const __amdgpu_buffer_rsrc_t rvs = make_rsrc(a.vs + (tile >= 0 ? tile * 16 : 0), tile >= 0 ? 64u : 0u);
+#pragma unroll
+    for (int j = 0; j < S::NI; ++j)
+      kr[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                            rk, (uint32_t)(j * 64 + lane) * 8u, 0, kCachePolicyNonTemporal));
+#pragma unroll
+    for (int j = 0; j < S::NI; ++j)
+      vr[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                            rv, (uint32_t)(j * 64 + lane) * 8u, 0, kCachePolicyNonTemporal));
+    sk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, (uint32_t)(lane & 15) * 4u, 0,
+                                                               kCachePolicyNonTemporal));
+    sv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, (uint32_t)(lane & 15) * 4u, 0,
+                                                               kCachePolicyNonTemporal));
+  };
 
   float m_run = -INFINITY, l_run = 0.f;
   float acc[G][S::CE];
@@ -261,11 +313,35 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
   const bool fuse = FUSE && a.k_new != nullptr && part == n_used - 1;
   const int t_new = (ctx - 1) & 15;
   u32x4 k_new_c = u32x4{0u, 0u, 0u, 0u}, v_new_c = u32x4{0u, 0u, 0u, 0u};
-  if (fuse) {
+  auto load_new = [&] {
     const size_t src = ((size_t)b * a.hkv + kvh) * S::RB + (lane % S::NC) * 16;
     k_new_c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.k_new) + src);
     v_new_c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.v_new) + src);
-  }
+  };
+  if (!F8 && fuse) load_new();
+  // fp8: the new row's codes (this lane's 8 values) and scales, quantised as
+  // kv_append does (the NC lanes of each group hold the whole row). The wave
+  // that processes the last block makes them there, just before it, so that
+  // nothing of the new row is held in registers through the loop.
+  u32x2 k_new_q = u32x2{0u, 0u}, v_new_q = u32x2{0u, 0u};
+  float k_new_s = 0.f, v_new_s = 0.f;
+  bool has_tail = false;   // fp8: this wave processed the sequence's last block
+  auto quantise_new = [&] {
+    if constexpr (F8) {
+      load_new();
+      const float ka = group_max<S::NC>(bf16x8_amax(k_new_c));
+      const float va = group_max<S::NC>(bf16x8_amax(v_new_c));
+      if (ka >= kZeroRowAmax) {
+        k_new_q = bf16x8_to_e4m3x8(k_new_c, kE4M3Max / ka);
+        k_new_s = ka / kE4M3Max;
+      }
+      if (va >= kZeroRowAmax) {
+        v_new_q = bf16x8_to_e4m3x8(v_new_c, kE4M3Max / va);
+        v_new_s = va / kE4M3Max;
+      }
+    }
+  };
+  float cur_sk = 0.f, cur_sv = 0.f;   // fp8: the block's row scales, lane l: token l % 16
   // One block. TAIL marks the sequence's last block, the only one that can be
   // partial or hold the appended token; every other block skips the masking
   // and substitution code entirely.
@@ -276,7 +352,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
 #pragma unroll
       for (int j = 0; j < S::NI; ++j) {
         const int tk = (j * 64 + lane) / S::NC;
-        if (fuse && tk == t_new) {
+        if (!F8 && fuse && tk == t_new) {
           kb[j] = k_new_c;
           vb[j] = v_new_c;
         }
@@ -300,12 +376,18 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       for (int cc = 0; cc < S::NCQ; ++cc) {
         const int c = qh * S::NCQ + cc;
         const u32x4 kk = *reinterpret_cast<const u32x4*>(kst + t * S::RB + ((c ^ (t % S::NC)) << 4));
-        chunk_dot<T>(kk, qv[cc], part_s);
+        chunk_dot<C>(kk, qv[cc], part_s);
       }
       float dot = (part_s[0] + part_s[1]) + (part_s[2] + part_s[3]);
       dot += dpp_f<kQuadXor1>(dot);                  // the other half of the head dim
       const bool valid = active && (!TAIL || lb * 16 + t < ctx);
-      s[sl] = valid ? dot * a.scale_log2 : -INFINITY;
+      if constexpr (F8) {
+        // the key row's scale multiplies its dot product
+        const float skt = __int_as_float(__builtin_amdgcn_ds_bpermute(t * 4, __float_as_int(cur_sk)));
+        s[sl] = valid ? dot * skt * a.scale_log2 : -INFINITY;
+      } else {
+        s[sl] = valid ? dot * a.scale_log2 : -INFINITY;
+      }
     }
 
     // online softmax over this block's tokens, per head (each token sits in
@@ -329,6 +411,17 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     ps = group_sum<S::LPH>(ps);
     l_run = l_run * alpha + ps;
     m_run = m_new;
+    float pw[S::SPL];   // the PV weights: p, times the value row's scale for fp8
+#pragma unroll
+    for (int sl = 0; sl < S::SPL; ++sl) {
+      pw[sl] = p[sl];
+      if constexpr (F8) {
+        const int t = tt + S::TPS * sl;
+        const float svt = __int_as_float(__builtin_amdgcn_ds_bpermute(t * 4, __float_as_int(cur_sv)));
+        // rows past the context may hold NaN scales; their weight is 0
+        pw[sl] = (!TAIL || lb * 16 + t < ctx) ? p[sl] * svt : 0.f;
+      }
+    }
     if (active && qh == 0) {
 #pragma unroll
       for (int sl = 0; sl < S::SPL; ++sl) {
@@ -338,7 +431,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
           // (j/2)*TPI + r, low half for even j
           const int jt = t / S::TPI, r = t % S::TPI;
           p16[((jt >> 1) * S::TPI + r) * (2 * G) + 2 * h + (jt & 1)] =
-              (uint16_t)(__float_as_uint(p[sl]) >> 16);
+              F8 ? (uint16_t)f32_to_bf16_bits(pw[sl]) : (uint16_t)(__float_as_uint(p[sl]) >> 16);
         } else {
           plds[t * G + h] = p[sl];
         }
@@ -399,52 +492,128 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     }
   };
 
-  for (;;) {
-    start_range();
+  // fp8: convert a ring slot's codes to the bf16 tile the shared path reads
+  // (with the new token's codes and scales in place for the tail block), then
+  // process it.
+  auto process8 = [&](auto tail_tag, u32x2 (&kr)[S::NI], u32x2 (&vr)[S::NI], float sk, float sv,
+                      int i) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    u32x4 kb[S::NI], vb[S::NI];
+#pragma unroll
+    for (int j = 0; j < S::NI; ++j) {
+      u32x2 kx = kr[j], vx = vr[j];
+      if constexpr (TAIL) {
+        if (fuse && (j * 64 + lane) / S::NC == t_new) {
+          kx = k_new_q;
+          vx = v_new_q;
+        }
+      }
+      kb[j] = e4m3x8_to_bf16x8(kx);
+      vb[j] = e4m3x8_to_bf16x8(vx);
+    }
+    cur_sk = sk;
+    cur_sv = sv;
+    if constexpr (TAIL) {
+      if (fuse && (lane & 15) == t_new) {
+        cur_sk = k_new_s;
+        cur_sv = v_new_s;
+      }
+    }
+    process(tail_tag, kb, vb, i);
+  };
+
+  // One range of blocks through the ring of PF blocks in flight.
+  auto run_range = [&] {
     // Ring of PF blocks in flight; a slot is refilled right after it is used.
     // A wave's blocks ascend, so only its last step can be the sequence's last
     // block: the loop runs the plain path only and the last step is peeled.
-    u32x4 kb[S::PF][S::NI], vb[S::PF][S::NI];
-#pragma unroll
-    for (int u = 0; u < S::PF; ++u) issue(kb[u], vb[u], u);
     const int n_main = n_my > 0 ? n_my - 1 : 0;
-    for (int i = 0; i < n_main; i += S::PF) {
+    if constexpr (F8) {
+      u32x2 kr[PF][S::NI], vr[PF][S::NI];
+      float skr[PF], svr[PF];
 #pragma unroll
-      for (int u = 0; u < S::PF; ++u) {
-        if (i + u < n_main) {
-          process(std::false_type{}, kb[u], vb[u], i + u);
-          // keep the refill of this slot after its use: hoisting the loads
-          // above the PV products would force a register copy of the tile
-          __builtin_amdgcn_sched_barrier(0);
-          issue(kb[u], vb[u], i + u + S::PF);
+      for (int u = 0; u < PF; ++u) issue8(kr[u], vr[u], skr[u], svr[u], u);
+      for (int i = 0; i < n_main; i += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          if (i + u < n_main) {
+            process8(std::false_type{}, kr[u], vr[u], skr[u], svr[u], i + u);
+            __builtin_amdgcn_sched_barrier(0);
+            issue8(kr[u], vr[u], skr[u], svr[u], i + u + PF);
+          }
+        }
+      }
+      if (n_my > 0) {
+        const int last = n_my - 1, slot = last % PF;
+        const bool tail = blk0 + w + last * NW == nblk - 1;
+        if (tail && fuse) {
+          quantise_new();
+          has_tail = true;
+        }
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          if (u == slot) {
+            if (tail)
+              process8(std::true_type{}, kr[u], vr[u], skr[u], svr[u], last);
+            else
+              process8(std::false_type{}, kr[u], vr[u], skr[u], svr[u], last);
+          }
+        }
+      }
+    } else {
+      u32x4 kb[S::PF][S::NI], vb[S::PF][S::NI];
+#pragma unroll
+      for (int u = 0; u < S::PF; ++u) issue(kb[u], vb[u], u);
+      for (int i = 0; i < n_main; i += S::PF) {
+#pragma unroll
+        for (int u = 0; u < S::PF; ++u) {
+          if (i + u < n_main) {
+            process(std::false_type{}, kb[u], vb[u], i + u);
+            // keep the refill of this slot after its use: hoisting the loads
+            // above the PV products would force a register copy of the tile
+            __builtin_amdgcn_sched_barrier(0);
+            issue(kb[u], vb[u], i + u + S::PF);
+          }
+        }
+      }
+      if (n_my > 0) {
+        const int last = n_my - 1, slot = last % S::PF;
+        const bool tail = blk0 + w + last * NW == nblk - 1;
+#pragma unroll
+        for (int u = 0; u < S::PF; ++u) {
+          if (u == slot) {
+            if (tail)
+              process(std::true_type{}, kb[u], vb[u], last);
+            else
+              process(std::false_type{}, kb[u], vb[u], last);
+          }
         }
       }
     }
-    if (n_my > 0) {
-      const int last = n_my - 1, slot = last % S::PF;
-      const bool tail = blk0 + w + last * NW == nblk - 1;
-#pragma unroll
-      for (int u = 0; u < S::PF; ++u) {
-        if (u == slot) {
-          if (tail)
-            process(std::true_type{}, kb[u], vb[u], last);
-          else
-            process(std::false_type{}, kb[u], vb[u], last);
-        }
-      }
+  };
+  run_range();
+  if constexpr (WHOLE) {
+    for (blk0 += S::MAX_PART; blk0 < blk_end; blk0 += S::MAX_PART) {
+      start_range();
+      run_range();
     }
-    if constexpr (!WHOLE) break;
-    blk0 += S::MAX_PART;
-    if (blk0 >= blk_end) break;
   }
 
-  // fused append: write the new token's row (lanes 0..NC-1: K, NC..2NC-1: V)
-  if (fuse && w == 0 && lane < 2 * S::NC) {
+  // fused append: write the new token's row (lanes 0..NC-1: K, NC..2NC-1: V;
+  // wave 0 for bf16 and fp32, the wave that made the codes for fp8)
+  if (fuse && (F8 ? has_tail : w == 0) && lane < 2 * S::NC) {
     const int blk = bt_row[nblk - 1];
     if ((unsigned)blk < (unsigned)a.num_blocks) {
-      const size_t dst = (((size_t)blk * a.hkv + kvh) * 16 + t_new) * S::RB + (lane % S::NC) * 16;
+      const size_t prow = ((size_t)blk * a.hkv + kvh) * 16 + t_new;
       uint8_t* base = const_cast<uint8_t*>(lane < S::NC ? kbase : vbase);
-      *reinterpret_cast<u32x4*>(base + dst) = lane < S::NC ? k_new_c : v_new_c;
+      if constexpr (F8) {
+        *reinterpret_cast<u32x2*>(base + prow * D + (lane % S::NC) * 8) =
+            lane < S::NC ? k_new_q : v_new_q;
+        if (lane % S::NC == 0) (lane < S::NC ? a.ks : a.vs)[prow] = lane < S::NC ? k_new_s : v_new_s;
+      } else {
+        *reinterpret_cast<u32x4*>(base + prow * S::RB + (lane % S::NC) * 16) =
+            lane < S::NC ? k_new_c : v_new_c;
+      }
     }
   }
 
@@ -481,7 +650,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     }
     const size_t row = (size_t)b * hq_all + kvh * G + hh;
     if (n_used == 1) {
-      store_out<T>(a.out, row * D + d, A / L);
+      store_out<C>(a.out, row * D + d, A / L);
     } else {
       a.ws_o[(row * a.n_part + part) * D + d] = A;
       if (d == 0) a.ws_ml[row * a.n_part + part] = make_float2(M, L);

@@ -14,10 +14,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Storage tag for bfloat16 elements (raw 16-bit patterns).
 struct bf16_tag {};
+// Storage tag for fp8 E4M3 codes with one fp32 scale per (token, kv head) row;
+// the kernels compute on them in bf16 (every E4M3 value is a bf16 value).
+struct fp8_tag {};
 
 template <typename T> struct ElemBytes;
 template <> struct ElemBytes<float> { static constexpr int value = 4; };
 template <> struct ElemBytes<bf16_tag> { static constexpr int value = 2; };
+template <> struct ElemBytes<fp8_tag> { static constexpr int value = 1; };
 
 // ---------------------------------------------------------------------------
 // Buffer resources. A raw (stride 0) buffer descriptor over [base, base+bytes):
@@ -56,6 +60,65 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// ---------------------------------------------------------------------------
+// fp8 E4M3 (OCP: bias 7, largest finite 448, S.1111.111 = NaN)
+// ---------------------------------------------------------------------------
+constexpr float kE4M3Max = 448.f;
+// Rows whose largest magnitude is below this are stored as zeros (scale 0), so
+// that 448 / amax stays finite.
+constexpr float kZeroRowAmax = 0x1p-100f;
+
+// Code of a finite value: nearest E4M3 value, ties to the even code (the even
+// mantissa), magnitudes above 448 clamped to 448; values that round to zero
+// give +0.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const float a = fminf(fabsf(y), kE4M3Max);
+  uint32_t code;
+  if (a < 0.015625f) {
+    // below 2^-6 the codes are the multiples of 2^-9 (scaling by 2^9 is exact)
+    code = (uint32_t)__builtin_rintf(a * 512.f);
+  } else {
+    // round the fp32 mantissa to 3 bits (ties to even), carrying into the
+    // exponent; then rebias the exponent from 127 to 7
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);
+    code = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
+  }
+  return (y < 0.f && code != 0u) ? (code | 0x80u) : code;
+}
+
+// Eight codes (little-endian bytes of two words) to eight bf16 values in four
+// words, exactly (the gfx950 conversion reads OCP E4M3).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(const u32x2& w) {
+  return u32x4{
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, true))};
+}
+
+// Eight bf16 values (four words) times inv, each coded to E4M3.
+__device__ __forceinline__ u32x2 bf16x8_to_e4m3x8(const u32x4& v, float inv) {
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[2 * i] = f32_to_e4m3(__uint_as_float(v[i] << 16) * inv);
+    c[2 * i + 1] = f32_to_e4m3(__uint_as_float(v[i] & 0xffff0000u) * inv);
+  }
+  return u32x2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+               c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+}
+
+// Largest magnitude of eight bf16 values (four words).
+__device__ __forceinline__ float bf16x8_amax(const u32x4& v) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    m = fmaxf(m, fmaxf(fabsf(__uint_as_float(v[i] << 16)),
+                       fabsf(__uint_as_float(v[i] & 0xffff0000u))));
+  return m;
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

@@ -8,13 +8,15 @@
 
 namespace kvc {
 
+// Bytes of one cached element (codes only for KVC_FP8).
 inline int dtype_bytes(int32_t dtype) {
-  return dtype == KVC_F32 ? 4 : dtype == KVC_BF16 ? 2 : 0;
+  return dtype == KVC_F32 ? 4 : dtype == KVC_BF16 ? 2 : dtype == KVC_FP8 ? 1 : 0;
 }
 
 inline bool head_dim_supported(int32_t dtype, int32_t d) {
   if (dtype == KVC_F32) return d == 16 || d == 32 || d == 64 || d == 128;
   if (dtype == KVC_BF16) return d == 32 || d == 64 || d == 128;
+  if (dtype == KVC_FP8) return d == 64 || d == 128;
   return false;
 }
 
@@ -22,6 +24,7 @@ inline bool head_dim_supported(int32_t dtype, int32_t d) {
 inline int check_cache(const kvc_cache* c) {
   if (!c || !c->k_cache || !c->v_cache) return KVC_ERR_NULL;
   if (dtype_bytes(c->dtype) == 0) return KVC_ERR_DTYPE;
+  if (c->dtype == KVC_FP8 && (!c->k_scale || !c->v_scale)) return KVC_ERR_NULL;
   if (c->block_size != 16) return KVC_ERR_UNSUPPORTED;
   if (c->num_blocks < 0 || c->num_kv_heads <= 0) return KVC_ERR_SHAPE;
   if (!head_dim_supported(c->dtype, c->head_dim)) return KVC_ERR_UNSUPPORTED;

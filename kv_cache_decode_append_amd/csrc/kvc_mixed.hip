@@ -337,6 +337,7 @@ extern "C" int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_
   using namespace kvc;
   int st = check_cache(cache);
   if (st != KVC_OK) return st;
+  if (cache->dtype == KVC_FP8) return KVC_ERR_UNSUPPORTED;
   if (!bt) return KVC_ERR_NULL;
   if (Hq <= 0 || Hq % cache->num_kv_heads != 0) return KVC_ERR_SHAPE;
   const int hkv = cache->num_kv_heads, D = cache->head_dim, G = Hq / hkv;
@@ -383,6 +384,8 @@ extern "C" int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_
   a.max_blocks = b.decode_max_blocks;
   a.max_ctx = b.decode_max_context;
   a.part_blocks = 1 << 30;
+  a.ks = nullptr;
+  a.vs = nullptr;
   a.n_part = 1;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
 

@@ -133,6 +133,7 @@ static int prefill_entry(const kvc_cache* cache, const void* q, const void* k, c
                          void* stream) {
   int st = check_cache(cache);
   if (st != KVC_OK) return st;
+  if (cache->dtype == KVC_FP8) return KVC_ERR_UNSUPPORTED;
   if (n_seqs < 0 || total_tokens < 0 || max_chunk_len < 0 || max_blocks < 0 || Hq <= 0)
     return KVC_ERR_SHAPE;
   if (Hq % cache->num_kv_heads != 0) return KVC_ERR_SHAPE;

@@ -174,3 +174,19 @@ def test_mixed_step_rejects_before_launch():
               prefill_total_tokens=10, prefill_max_chunk=10, prefill_block_table=1,
               prefill_max_blocks=4, out_prefill=None)
     assert f(byref, ctypes.byref(_mixed(**pf)), 4, 0.1, 1, 1 << 30, None) == -1
+
+
+def test_fp8_cache_rules():
+    c = _cache(dtype=2, head_dim=64)                  # no scale pools
+    byref = ctypes.byref(c)
+    assert LIB.kvc_kv_append(byref, 1, 1, 1, 4, None) == -1
+    c = _cache(dtype=2, head_dim=32, k_scale=1, v_scale=1)
+    assert LIB.kvc_kv_append(ctypes.byref(c), 1, 1, 1, 4, None) == -4
+    c = _cache(dtype=2, head_dim=64, k_scale=1, v_scale=1)
+    byref = ctypes.byref(c)
+    assert LIB.kvc_kv_append(byref, 1, 1, 1, 0, None) == 0
+    # prefill and the mixed step do not take an fp8 cache
+    assert LIB.kvc_chunked_prefill_attention(byref, 1, 1, 1, 1, 1, 1, 16, 16, 1, 1, 1, 0.1, 1,
+                                             None) == -4
+    assert LIB.kvc_mixed_step_attention(byref, ctypes.byref(_mixed()), 1, 0.1, 1, 256, None) == -4
+    assert kvc.KVC_FP8 == 2

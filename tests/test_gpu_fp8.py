@@ -1,0 +1,196 @@
+"""GPU parity for the fp8 (E4M3, per-row scales) KV cache.
+
+* kv_append: codes and scales bit for bit against the oracle's quantisation
+  of the same bf16 rows (zero rows, tiny and large magnitudes, skipped slots,
+  a NaN-filled pool around them);
+* decode: the kernel's attention over the quantised cache against the
+  oracle's attention over the same dequantised values (fp64), with the bf16
+  tolerance, for every G and both head sizes, split-K included;
+* the fused append + decode launch against append then decode, bit for bit;
+* the quantisation error itself (fp8 cache against the unquantised bf16
+  values) within its analytic bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as OA
+from oracle import bf16 as OB
+from oracle import quant as OQ
+from tests.gpu_cases import FILL, assert_close, say
+
+pytestmark = pytest.mark.gpu
+F8 = torch.float8_e4m3fn
+
+
+@pytest.fixture(scope="module")
+def kvc():
+    import kv_cache_decode_append_amd as m
+    return m
+
+
+def _bf16(x):
+    """fp32 values rounded to bf16 (as float32), the rows the cache is given."""
+    return OB.round_bf16(np.asarray(x, np.float32)).astype(np.float32)
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).cuda()
+
+
+@pytest.mark.parametrize("Hkv,D", [(1, 64), (8, 128), (3, 64)])
+def test_append_codes_and_scales_bitwise(kvc, Hkv, D):
+    rng = np.random.default_rng(60 + D + Hkv)
+    T, nb = 300, 40
+    x = rng.standard_normal((2, T, Hkv, D)).astype(np.float32)
+    x *= rng.choice([1e-6, 1e-3, 0.5, 3.0, 1e3], size=(2, T, Hkv, 1)).astype(np.float32)
+    x[:, 7] = 0.0                                   # zero rows
+    x[:, 8, :, 5] = 0.0
+    x[0, 9, 0, :] = np.float32(2.0 ** -110)         # below the zero-row limit: stored as zeros
+    x[1, 9, Hkv - 1, :2] = np.float32(2.0 ** -90)   # tiny but above it
+    x = _bf16(x)
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    slots[[3, 50, 51]] = -1                         # skipped tokens
+    say(f"fp8 append: {T} rows, Hkv {Hkv}, D {D}")
+    cache = kvc.PagedKVCache.allocate(nb, Hkv, D, F8, fill_bits=FILL)
+    kvc.kv_append(cache, torch.from_numpy(slots).cuda(), _dev(x[0]), _dev(x[1]))
+    torch.cuda.synchronize()
+    assert int(cache.err_flag.item()) == 0
+    kc = cache.k_cache.view(torch.uint8).cpu().numpy()
+    vc = cache.v_cache.view(torch.uint8).cpu().numpy()
+    ks, vs = cache.k_scale.cpu().numpy(), cache.v_scale.cpu().numpy()
+    written = np.zeros((nb * 16,), bool)
+    for which, pool, sc in ((0, kc, ks), (1, vc, vs)):
+        codes, scales = OQ.quantize_rows(x[which])
+        for t in range(T):
+            s = slots[t]
+            if s < 0:
+                continue
+            written[s] = True
+            assert np.array_equal(pool[s // 16, :, s % 16, :], codes[t]), (which, t)
+            assert np.array_equal(sc[s // 16, :, s % 16].view(np.uint32),
+                                  scales[t].view(np.uint32)), (which, t)
+    # rows not written keep the sentinel
+    for s in np.flatnonzero(~written)[:50]:
+        assert np.all(kc[s // 16, :, s % 16, :] == 0xFF)
+        assert np.all(np.isnan(ks[s // 16, :, s % 16]))
+
+
+class Fp8Case:
+    def __init__(self, wid, Hq, Hkv, D, ctx, seed_extra=0):
+        self.w = W.small_workload(f"fp8-{wid}", wid, B=len(ctx), Hq=Hq, Hkv=Hkv, D=D, dtype="bf16",
+                                  sigma=0.5)
+        self.ctx = np.asarray(ctx, np.int64)
+        self.nb = int(sum(W.blocks_for(int(c)) for c in self.ctx)) + 5
+        self.bt = W.block_tables(self.w, self.ctx, self.nb, seed_extra=seed_extra)
+        self.vals = [W.sequence_values(self.w, b, int(n), 1) for b, n in enumerate(self.ctx)]
+        # the bf16 rows the cache is given, and what the quantised cache holds
+        self.kb = [_bf16(v[0]) for v in self.vals]
+        self.vb = [_bf16(v[1]) for v in self.vals]
+        self.qb = np.stack([_bf16(v[2][0]) for v in self.vals])
+        self.kq = [OQ.dequantize_rows(*OQ.quantize_rows(k)) for k in self.kb]
+        self.vq = [OQ.dequantize_rows(*OQ.quantize_rows(v)) for v in self.vb]
+
+    def fill(self, kvc, upto_last=True):
+        """Cache holding positions 0 .. ctx - 2 (or - 1 with upto_last)."""
+        cache = kvc.PagedKVCache.allocate(self.nb, self.w.Hkv, self.w.D, F8, fill_bits=FILL)
+        btd = torch.from_numpy(self.bt).cuda()
+        n_of = [int(c) - (0 if upto_last else 1) for c in self.ctx]
+        rows = [b for b in range(len(self.ctx)) if n_of[b] > 0]
+        seq = np.concatenate([np.full(n_of[b], b, np.int32) for b in rows])
+        pos = np.concatenate([np.arange(n_of[b], dtype=np.int32) for b in rows])
+        s = kvc.slot_mapping(btd, self.nb, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(),
+                             err_flag=cache.err_flag)
+        kvc.kv_append(cache, s, _dev(np.concatenate([self.kb[b][:n_of[b]] for b in rows])),
+                      _dev(np.concatenate([self.vb[b][:n_of[b]] for b in rows])))
+        return cache, btd
+
+    def oracle(self, b, quantised=True):
+        k = self.kq[b] if quantised else self.kb[b].astype(np.float64)
+        v = self.vq[b] if quantised else self.vb[b].astype(np.float64)
+        return OA.attend_row(self.qb[b].astype(np.float64), k, v, OA.default_scale(self.w.D))
+
+
+CASES = [
+    (32, 8, 128, [1, 2, 16, 17, 100, 2049, 5000]),     # G = 4, the serving shape
+    (8, 8, 128, [3, 33, 700, 4100]),                    # G = 1
+    (16, 8, 128, [20, 300, 1200]),                      # G = 2
+    (64, 8, 128, [15, 640, 3000]),                      # G = 8
+    (8, 2, 64, [1, 31, 2500, 257]),                     # G = 4, D 64
+    (16, 2, 64, [9, 160, 6000]),                        # G = 8, D 64
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,ctx", CASES, ids=[f"{c[0]}/{c[1]}/{c[2]}" for c in CASES])
+def test_decode_over_fp8_cache_matches_oracle(kvc, Hq, Hkv, D, ctx):
+    case = Fp8Case(500 + Hq + D, Hq, Hkv, D, ctx)
+    say(f"fp8 decode {Hq}/{Hkv}/{D}: ctx {ctx}")
+    cache, btd = case.fill(kvc)
+    out = kvc.paged_decode_attention(cache, _dev(case.qb), btd,
+                                     torch.from_numpy(case.ctx.astype(np.int32)).cuda(),
+                                     int(case.ctx.max()))
+    torch.cuda.synchronize()
+    assert int(cache.err_flag.item()) == 0
+    got = out.float().cpu().numpy()
+    worst = 0.0
+    for b in range(len(ctx)):
+        worst = max(worst, assert_close(got[b], case.oracle(b), "bf16", f"fp8 decode row {b}"))
+    say(f"  max abs err {worst:.2e}")
+
+
+def test_fused_append_decode_equals_append_then_decode(kvc):
+    case = Fp8Case(560, 32, 8, 128, [1, 2, 16, 17, 31, 400, 3000, 2048], seed_extra=3)
+    say("fp8 fused append + decode vs append then decode")
+    ctx = torch.from_numpy(case.ctx.astype(np.int32)).cuda()
+    mc = int(case.ctx.max())
+    a, btd = case.fill(kvc, upto_last=False)
+    k_new = _dev(np.stack([k[-1] for k in case.kb]))
+    v_new = _dev(np.stack([v[-1] for v in case.vb]))
+    out_fused = kvc.decode_append_attention(a, _dev(case.qb), k_new, v_new, btd, ctx, mc)
+    b_cache, _ = case.fill(kvc, upto_last=True)
+    out_ref = kvc.paged_decode_attention(b_cache, _dev(case.qb), btd, ctx, mc)
+    torch.cuda.synchronize()
+    assert torch.equal(out_fused.view(torch.int16), out_ref.view(torch.int16))
+    assert torch.equal(a.k_cache.view(torch.uint8), b_cache.k_cache.view(torch.uint8))
+    assert torch.equal(a.v_cache.view(torch.uint8), b_cache.v_cache.view(torch.uint8))
+    used = torch.from_numpy(np.unique(case.bt[case.bt >= 0]).astype(np.int64)).cuda()
+    for x, y in ((a.k_scale, b_cache.k_scale), (a.v_scale, b_cache.v_scale)):
+        assert torch.equal(x.index_select(0, used).view(torch.int32),
+                           y.index_select(0, used).view(torch.int32))
+    got = out_fused.float().cpu().numpy()
+    for b in range(len(case.ctx)):
+        assert_close(got[b], case.oracle(b), "bf16", f"fused fp8 row {b}")
+
+
+def test_quantisation_error_within_its_bound(kvc):
+    """Attention over the fp8 cache against attention over the unquantised
+    bf16 rows. Each dequantised value is within 1/16 of its magnitude (or
+    2^-10 of its row scale below the normal range), so a logit moves by at
+    most delta = scale * sum_d |q_d| err_k,d, the softmax weights by at most a
+    factor exp(+-2 delta), and the output by at most
+    max|v| (exp(2 delta) - 1) + max err_v; the kernel's own rounding adds the
+    bf16 tolerance."""
+    case = Fp8Case(570, 32, 8, 128, [50, 500, 2000, 6000])
+    cache, btd = case.fill(kvc)
+    out = kvc.paged_decode_attention(cache, _dev(case.qb), btd,
+                                     torch.from_numpy(case.ctx.astype(np.int32)).cuda(),
+                                     int(case.ctx.max()))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    scale = OA.default_scale(case.w.D)
+    G = case.w.Hq // case.w.Hkv
+    worst_rel = 0.0
+    for b in range(len(case.ctx)):
+        ref = case.oracle(b, quantised=False)
+        kerr = np.abs(case.kq[b] - case.kb[b])          # [n, Hkv, D]
+        verr = np.abs(case.vq[b] - case.vb[b])
+        for hq in range(case.w.Hq):
+            h = hq // G
+            delta = scale * np.max(np.abs(case.qb[b, hq]) @ kerr[:, h, :].T)
+            vmax = np.max(np.abs(case.vb[b][:, h, :]))
+            bound = vmax * (np.exp(2 * delta) - 1) + np.max(verr[:, h, :]) + 1e-2
+            err = np.max(np.abs(got[b, hq] - ref[hq]))
+            assert err <= bound, (b, hq, err, bound)
+            worst_rel = max(worst_rel, err / max(np.max(np.abs(ref[hq])), 1e-6))
+    say(f"fp8 vs bf16 cache: worst error / max|out| = {worst_rel:.3e}")
