@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--workload", default="c3-decode",
                     choices=["c3-decode", "c3-fp8", "c4-mixed", "c5-decode", "c5-prefill",
-                             "prefix-warm", "queue-replay"])
+                             "c5-prefill-fp8", "prefix-warm", "queue-replay"])
     ap.add_argument("--direct-steps", type=int, default=400,
                     help="queue-replay: leading steps of each continuous plan run for real")
     return ap.parse_args()
@@ -153,6 +153,8 @@ def main():
         return bench_c5_decode(args)
     if args.workload == "c5-prefill":
         return bench_c5_prefill(args)
+    if args.workload == "c5-prefill-fp8":
+        return bench_c5_prefill(args, fp8=True)
     if args.workload == "prefix-warm":
         return bench_prefix_warm(args)
     if args.workload == "c4-mixed":
@@ -304,13 +306,7 @@ def bench_c3_fp8(args):
     caches = []
     for layer in range(L):
         c = kvc.PagedKVCache.allocate(nb, Hkv, D, torch.float8_e4m3fn, device=dev)
-        for pool in (c.k_cache, c.v_cache):
-            # finite codes: magnitude field 0x00..0x7E, either sign
-            code = torch.randint(0, 0x7F, pool.shape, generator=g, device=dev, dtype=torch.int32)
-            sign = torch.randint(0, 2, pool.shape, generator=g, device=dev, dtype=torch.int32)
-            pool.view(torch.uint8).copy_((code | (sign << 7)).to(torch.uint8))
-        c.k_scale.uniform_(0.5 / 448, 2.0 / 448, generator=g)
-        c.v_scale.uniform_(0.5 / 448, 2.0 / 448, generator=g)
+        fill_fp8_pools(c, g)
         caches.append(c)
     q = [torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5, generator=g)
          for _ in range(L)]
@@ -423,10 +419,22 @@ def bench_c5_decode(args):
     print(json.dumps(res), flush=True)
 
 
-def bench_c5_prefill(args):
+def fill_fp8_pools(cache, g=None):
+    """Finite random E4M3 codes and row scales (about unit-sized values)."""
+    import torch
+    for pool in (cache.k_cache, cache.v_cache):
+        code = torch.randint(0, 0x7F, pool.shape, generator=g, device=pool.device, dtype=torch.int32)
+        sign = torch.randint(0, 2, pool.shape, generator=g, device=pool.device, dtype=torch.int32)
+        pool.view(torch.uint8).copy_((code | (sign << 7)).to(torch.uint8))
+    cache.k_scale.uniform_(0.5 / 448, 2.0 / 448, generator=g)
+    cache.v_scale.uniform_(0.5 / 448, 2.0 / 448, generator=g)
+
+
+def bench_c5_prefill(args, fp8=False):
     """8 sequences, each a 2,048-token chunk over a 30,000-token cached prefix
     (chunk K/V write + causal attention on MFMA). Algorithmic work counts only
-    unmasked (query, key) pairs at 4 * head_dim flop each."""
+    unmasked (query, key) pairs at 4 * head_dim flop each. With fp8 the cache
+    holds E4M3 codes and row scales (dequantised to bf16 as tiles are staged)."""
     import torch
 
     import kv_cache_decode_append_amd as kvc
@@ -439,9 +447,13 @@ def bench_c5_prefill(args):
     total = np.full(n, P + C)
     nb = n * W.blocks_for(P + C)
     bt = torch.from_numpy(W.block_tables(w, total, nb)).to(dev)
-    cache = kvc.PagedKVCache.allocate(nb, Hkv, D, torch.bfloat16, device=dev)
-    cache.k_cache.normal_(0, 0.5)
-    cache.v_cache.normal_(0, 0.5)
+    if fp8:
+        cache = kvc.PagedKVCache.allocate(nb, Hkv, D, torch.float8_e4m3fn, device=dev)
+        fill_fp8_pools(cache)
+    else:
+        cache = kvc.PagedKVCache.allocate(nb, Hkv, D, torch.bfloat16, device=dev)
+        cache.k_cache.normal_(0, 0.5)
+        cache.v_cache.normal_(0, 0.5)
     q = torch.empty(n * C, Hq, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
     k = torch.empty(n * C, Hkv, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
     v = torch.empty_like(k)
@@ -454,10 +466,12 @@ def bench_c5_prefill(args):
     pairs = n * Hq * (C * P + C * (C + 1) // 2)
     flop = pairs * 4 * D
     tf = flop / (ms * 1e-3) / 1e12
-    res = _base_line(args, "chunked-prefill attention TFLOP/s, 8 x 2,048 over a 30,000 prefix",
-                     round(tf, 1), "TFLOP/s", ms, "bf16",
+    tag = ", fp8 E4M3 cache" if fp8 else ""
+    res = _base_line(args, "chunked-prefill attention TFLOP/s, 8 x 2,048 over a 30,000 prefix" + tag,
+                     round(tf, 1), "TFLOP/s", ms, "fp8-e4m3 cache, bf16 compute" if fp8 else "bf16",
                      {"workload": "chunked prefill, 8 sequences x 2,048-token chunk over a "
-                                  "30,000-token cached prefix, GQA 32/8, head_dim 128, bf16",
+                                  "30,000-token cached prefix, GQA 32/8, head_dim 128, "
+                                  + ("fp8 E4M3 cache with row scales" if fp8 else "bf16"),
                       "n_seqs": n, "chunk": C, "prefix": P},
                      {"bound": "mfma", "kernel": "chunk_append_kernel + prefill_attention_kernel",
                       "achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",

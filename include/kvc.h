@@ -52,9 +52,11 @@
  *     said") names quantising the cache for memory headroom at a small
  *     accuracy cost and gives no scheme; this one keeps each appended row
  *     independent of the rows after it. Queries, new K/V and outputs are bf16.
- *     Supported by kvc_kv_append, kvc_paged_decode_attention and
- *     kvc_decode_append_attention with head_dim 64 or 128; the prefill and
- *     mixed-step calls return KVC_ERR_UNSUPPORTED for such a cache.
+ *     Supported by kvc_kv_append, kvc_paged_decode_attention,
+ *     kvc_decode_append_attention and the chunked-prefill calls (which write
+ *     the chunk quantised and dequantise tiles to bf16 as they stage them)
+ *     with head_dim 64 or 128; kvc_mixed_step_attention returns
+ *     KVC_ERR_UNSUPPORTED for such a cache.
  */
 #ifndef KVC_H
 #define KVC_H

@@ -136,9 +136,72 @@ __global__ void chunk_append_kernel(uint8_t* __restrict__ kc, uint8_t* __restric
   if (bad && h == 0 && c == 0) flag_error(err, bad);
 }
 
+// fp8 cache: the chunk rows quantised as kv_append_fp8_kernel does, one 8-value
+// chunk per thread, the NCB threads of a row reducing its amax together.
+// grid = (ceil(max_chunk * hkv * NCB / 256), n_seqs).
+template <int NCB>
+__global__ __launch_bounds__(256) void chunk_append_fp8_kernel(
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ ks,
+    float* __restrict__ vs, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
+    const int32_t* __restrict__ block_table, int32_t max_blocks, int32_t num_blocks, int32_t hkv,
+    int32_t total, int32_t max_chunk, int32_t* err) {
+  const int s = blockIdx.y;
+  const int32_t t0 = cu[s], C = cu[s + 1] - t0, p0 = prefix[s];
+  const bool ok = chunk_ok(t0, C, p0, total, max_chunk);
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = i / NCB;                 // (r, h)
+  const int32_t c = (int32_t)(i % NCB);
+  const int32_t r = (int32_t)(row / hkv);
+  const int32_t h = (int32_t)(row - (int64_t)r * hkv);
+  const bool in = ok && r < C;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int64_t src = (((int64_t)(t0 + r) * hkv + h) * NCB + c) * 16;
+  const u32x4 kx = in ? *reinterpret_cast<const u32x4*>(k + src) : zero;
+  const u32x4 vx = in ? *reinterpret_cast<const u32x4*>(v + src) : zero;
+  const float ka = group_max<NCB>(bf16x8_amax(kx));
+  const float va = group_max<NCB>(bf16x8_amax(vx));
+  if (!ok) {
+    if (i == 0) flag_error(err, KVC_DEVERR_CONTEXT);
+    return;
+  }
+  if (!in) return;
+  const int32_t p = p0 + r, lb = p >> 4;
+  if (lb >= max_blocks) {
+    if (h == 0 && c == 0) flag_error(err, KVC_DEVERR_CONTEXT);
+    return;
+  }
+  const int32_t blk = block_table[(int64_t)s * max_blocks + lb];
+  if (blk < 0 || blk >= num_blocks) {
+    if (h == 0 && c == 0) flag_error(err, KVC_DEVERR_BLOCK_ID);
+    return;
+  }
+  const int64_t prow = ((int64_t)blk * hkv + h) * 16 + (p & 15);
+  const bool kz = !(ka >= kZeroRowAmax), vz = !(va >= kZeroRowAmax);
+  *reinterpret_cast<u32x2*>(kc + prow * (NCB * 8) + c * 8) =
+      kz ? u32x2{0u, 0u} : bf16x8_to_e4m3x8(kx, kE4M3Max / ka);
+  *reinterpret_cast<u32x2*>(vc + prow * (NCB * 8) + c * 8) =
+      vz ? u32x2{0u, 0u} : bf16x8_to_e4m3x8(vx, kE4M3Max / va);
+  if (c == 0) {
+    ks[prow] = kz ? 0.f : ka / kE4M3Max;
+    vs[prow] = vz ? 0.f : va / kE4M3Max;
+  }
+}
+
 int launch_chunk_append(const kvc_cache* c, const void* k, const void* v, int32_t n_seqs,
                         const int32_t* cu, const int32_t* prefix, int32_t total, int32_t max_chunk,
                         const int32_t* block_table, int32_t max_blocks, hipStream_t st) {
+  if (c->dtype == KVC_FP8) {
+    const int ncb = c->head_dim / 8;
+    const int64_t per_seq = (int64_t)max_chunk * c->num_kv_heads * ncb;
+    if (per_seq == 0 || n_seqs == 0) return KVC_OK;
+    auto kern = ncb == 16 ? chunk_append_fp8_kernel<16> : chunk_append_fp8_kernel<8>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(per_seq, 256), (unsigned)n_seqs), dim3(256), 0,
+                       st, (uint8_t*)c->k_cache, (uint8_t*)c->v_cache, c->k_scale, c->v_scale,
+                       (const uint8_t*)k, (const uint8_t*)v, cu, prefix, block_table, max_blocks,
+                       c->num_blocks, c->num_kv_heads, total, max_chunk, c->err_flag);
+    return launch_status();
+  }
   const int nc = c->head_dim * dtype_bytes(c->dtype) / 16;
   const int64_t per_seq = (int64_t)max_chunk * c->num_kv_heads * nc;
   if (per_seq == 0 || n_seqs == 0) return KVC_OK;

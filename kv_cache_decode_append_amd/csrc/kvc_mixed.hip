@@ -411,6 +411,8 @@ extern "C" int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_
   p.scale_log2 = a.scale_log2;
   p.ws_o = nullptr;
   p.ws_ml = nullptr;
+  p.ks = nullptr;
+  p.vs = nullptr;
 
   m.k_pf = reinterpret_cast<const uint8_t*>(b.k_prefill);
   m.v_pf = reinterpret_cast<const uint8_t*>(b.v_prefill);

@@ -13,7 +13,7 @@ namespace kvc {
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[PfShape<T, D, G>::SMEM];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[PfShape<PfComputeT<T>, D, G>::SMEM];
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
   // each XCD a contiguous run of work items; the query tiles of one (sequence,
   // kv head) then share one L2 while they sweep the same keys.
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(64) void prefill_merge_kernel(PrefillArgs a, int32_
       if (ml[i].x != -INFINITY)
         acc += __builtin_amdgcn_exp2f(ml[i].x - M) * a.ws_o[(row * a.n_split + i) * D + d];
     const float v = acc * inv;
-    if constexpr (ElemBytes<T>::value == 4) {
+    if constexpr (ElemBytes<PfComputeT<T>>::value == 4) {
       reinterpret_cast<float*>(a.out)[row * D + d] = v;
     } else {
       reinterpret_cast<uint16_t*>(a.out)[row * D + d] = (uint16_t)f32_to_bf16_bits(v);
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(64) void prefill_merge_kernel(PrefillArgs a, int32_
 
 template <typename T, int D, int G>
 int launch_prefill(PrefillArgs a, int n_seqs, int max_chunk, hipStream_t st) {
-  using S = PfShape<T, D, G>;
+  using S = PfShape<PfComputeT<T>, D, G>;
   a.n_qt = (max_chunk + S::MP - 1) / S::MP;
   a.n_work = a.n_qt * a.n_split * a.hkv * n_seqs;
   const int grid = (a.n_work + 7) / 8 * 8;           // whole XCD rounds
@@ -84,11 +84,16 @@ int dispatch_prefill(const PrefillArgs& a, int dtype, int D, int G, int n, int m
       case 64: return prefill_g<float, 64>(a, G, n, mc, st);
       case 128: return prefill_g<float, 128>(a, G, n, mc, st);
     }
-  } else {
+  } else if (dtype == KVC_BF16) {
     switch (D) {
       case 32: return prefill_g<bf16_tag, 32>(a, G, n, mc, st);
       case 64: return prefill_g<bf16_tag, 64>(a, G, n, mc, st);
       case 128: return prefill_g<bf16_tag, 128>(a, G, n, mc, st);
+    }
+  } else {
+    switch (D) {
+      case 64: return prefill_g<fp8_tag, 64>(a, G, n, mc, st);
+      case 128: return prefill_g<fp8_tag, 128>(a, G, n, mc, st);
     }
   }
   return KVC_ERR_UNSUPPORTED;
@@ -133,7 +138,6 @@ static int prefill_entry(const kvc_cache* cache, const void* q, const void* k, c
                          void* stream) {
   int st = check_cache(cache);
   if (st != KVC_OK) return st;
-  if (cache->dtype == KVC_FP8) return KVC_ERR_UNSUPPORTED;
   if (n_seqs < 0 || total_tokens < 0 || max_chunk_len < 0 || max_blocks < 0 || Hq <= 0)
     return KVC_ERR_SHAPE;
   if (Hq % cache->num_kv_heads != 0) return KVC_ERR_SHAPE;
@@ -170,6 +174,8 @@ static int prefill_entry(const kvc_cache* cache, const void* q, const void* k, c
   a.n_split = sp.n_split;
   a.split_tiles = sp.split_tiles;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.ks = cache->k_scale;
+  a.vs = cache->v_scale;
   a.ws_o = reinterpret_cast<float*>(workspace);
   a.ws_ml = need > 0 ? reinterpret_cast<float2*>(reinterpret_cast<uint8_t*>(workspace) +
                                                   (size_t)total_tokens * Hq * sp.n_split *

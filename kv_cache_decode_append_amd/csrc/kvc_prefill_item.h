@@ -30,6 +30,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "kvc.h"
 #include "kvc_append.h"
 #include "kvc_device.h"
@@ -65,6 +67,10 @@ template <> struct PfMfma<float> {
 template <bool BF16> struct PfP;
 template <> struct PfP<true> { struct Tile { u32x4 v[2][kRowTiles]; }; };
 template <> struct PfP<false> { struct Tile { float v[4][kRowTiles][4]; }; };
+
+// Type the prefill computes in: fp8 tiles are dequantised to bf16 in LDS.
+template <typename T>
+using PfComputeT = std::conditional_t<std::is_same_v<T, fp8_tag>, bf16_tag, T>;
 
 template <typename T, int D, int G>
 struct PfShape {
@@ -113,6 +119,8 @@ struct PrefillArgs {
   float scale_log2;
   float* ws_o;        // split partials: [total][Hq][n_split][D] fp32, unnormalised
   float2* ws_ml;      // [total][Hq][n_split] (running max in log2 units, row sum)
+  const float* ks;    // fp8 caches: row scales [num_blocks][hkv][16] of K and V
+  const float* vs;
 };
 
 template <typename T>
@@ -136,9 +144,14 @@ __device__ __forceinline__ void store4<bf16_tag>(void* out, size_t idx, const f3
 template <typename T, int D, int G>
 __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uint8_t* smem,
                                              int tid = threadIdx.x) {
-  using S = PfShape<T, D, G>;
-  using M = PfMfma<T>;
+  // fp8 caches are dequantised to bf16 as their tiles are staged into LDS
+  // (code * row scale, rounded to bf16) and then take the bf16 path
+  constexpr bool F8 = std::is_same_v<T, fp8_tag>;
+  using CT = PfComputeT<T>;
+  using S = PfShape<CT, D, G>;
+  using M = PfMfma<CT>;
   using Frag = typename M::Frag;
+  constexpr int RB_MEM = F8 ? D : S::RB;              // bytes of one cached row
   int32_t* bt_lds = reinterpret_cast<int32_t*>(smem + S::TILES);
   const int qt = work % a.n_qt;
   const int sp = (work / a.n_qt) % a.n_split;
@@ -260,11 +273,12 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
   // 16 bytes (chunk c) of key `key` of tile kt. An absent key loads from the
   // pool's first row (always valid) and is zeroed when stored to LDS, so no
   // wait for the load lands here.
-  struct Row16 { int64_t off; bool ok; };
+  struct Row16 { int64_t off; bool ok; int64_t row; };
   auto locate = [&](int kt, int key, bool cached) -> Row16 {
     const int r = block_row(kt * 4 + (key >> 4), cached);
     const bool ok = r >= 0 && kt * kKeyTile + key < kv_len;
-    return {ok ? (int64_t)r * (16 * S::RB) + (key & 15) * S::RB : 0, ok};
+    return {ok ? (int64_t)r * (16 * RB_MEM) + (key & 15) * RB_MEM : 0, ok,
+            ok ? (int64_t)r * 16 + (key & 15) : 0};
   };
   auto zero_unless = [](bool ok, const u32x4& v) { return ok ? v : u32x4{0u, 0u, 0u, 0u}; };
 
@@ -274,6 +288,15 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
   constexpr bool kAllV = S::V_UNITS % kPfThreads == 0;
   u32x4 kr[S::KPT], vr[S::VPT][S::VCH];
   bool kok[S::KPT], vok[S::VPT][S::VCH];
+  // fp8: the codes of the same (key, 8 values) units and their rows' scales
+  u32x2 kr8[S::KPT], vr8[S::VPT][S::VCH];
+  float ksc[S::KPT], vsc[S::VPT][S::VCH];
+  auto dequant = [](const u32x2& w, float sc) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
+    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
+    return u32x4{pack_bf16x2(a[0] * sc, a[1] * sc), pack_bf16x2(b[0] * sc, b[1] * sc),
+                 pack_bf16x2(c[0] * sc, c[1] * sc), pack_bf16x2(d[0] * sc, d[1] * sc)};
+  };
   // A wave's K units cover 64 / NC <= 16 consecutive keys starting at a
   // multiple of 64 / NC, so they sit in one block: its base is a scalar, and
   // the lane's offset inside the block does not change between tiles. A unit
@@ -288,9 +311,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
       const int key = has ? ci / S::NC : 0;
       const int r = __builtin_amdgcn_readfirstlane(
           block_row(kt * 4 + __builtin_amdgcn_readfirstlane(key >> 4), cached));
-      const uint8_t* base = kbase + (r >= 0 ? (int64_t)r * (16 * S::RB) : 0);
+      const uint8_t* base = kbase + (r >= 0 ? (int64_t)r * (16 * RB_MEM) : 0);
       kok[j] = has && r >= 0 && kt * kKeyTile + key < kv_len;
-      kr[j] = *reinterpret_cast<const u32x4*>(base + (key & 15) * S::RB + (ci % S::NC) * 16);
+      if constexpr (F8) {
+        kr8[j] = *reinterpret_cast<const u32x2*>(base + (key & 15) * RB_MEM + (ci % S::NC) * 8);
+        ksc[j] = a.ks[(r >= 0 ? (int64_t)r * 16 : 0) + (key & 15)];
+      } else {
+        kr[j] = *reinterpret_cast<const u32x4*>(base + (key & 15) * S::RB + (ci % S::NC) * 16);
+      }
     }
   };
   auto load_v = [&](int kt) {
@@ -307,7 +335,12 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
         const int c = S::BF16 ? u / (kKeyTile / 2) : u % S::NC;
         const Row16 rw = locate(kt, key, cached);
         vok[j][x] = has && rw.ok;
-        vr[j][x] = *reinterpret_cast<const u32x4*>(vbase + rw.off + c * 16);
+        if constexpr (F8) {
+          vr8[j][x] = *reinterpret_cast<const u32x2*>(vbase + rw.off + c * 8);
+          vsc[j][x] = a.vs[rw.row];
+        } else {
+          vr[j][x] = *reinterpret_cast<const u32x4*>(vbase + rw.off + c * 16);
+        }
       }
     }
   };
@@ -317,6 +350,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
       const int ci = tid + j * kPfThreads;
       if (kAllK || ci < S::K_UNITS) {
         const int key = ci / S::NC, c = ci % S::NC;
+        if constexpr (F8) kr[j] = dequant(kr8[j], ksc[j]);
         *reinterpret_cast<u32x4*>(k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)) =
             zero_unless(kok[j], kr[j]);
       }
@@ -327,6 +361,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
     for (int j = 0; j < S::VPT; ++j) {
       const int u = tid + j * kPfThreads;
       if (!kAllV && u >= S::V_UNITS) continue;
+      if constexpr (F8) {
+#pragma unroll
+        for (int x = 0; x < S::VCH; ++x) vr[j][x] = dequant(vr8[j][x], vsc[j][x]);
+      }
       const u32x4 v0 = zero_unless(vok[j][0], vr[j][0]);
       const u32x4 v1 = zero_unless(vok[j][S::VCH - 1], vr[j][S::VCH - 1]);
       if constexpr (S::BF16) {
@@ -643,7 +681,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
     if (a.n_split == 1) {
       const float inv = 1.f / l_row[n];
 #pragma unroll
-      for (int dt = 0; dt < S::DT; ++dt) store4<T>(a.out, row * D + dt * 16 + g * 4, o[n][dt], inv);
+      for (int dt = 0; dt < S::DT; ++dt) store4<CT>(a.out, row * D + dt * 16 + g * 4, o[n][dt], inv);
     } else {
       // partial of this key range: unnormalised accumulators, running max, row sum
       const size_t pr = row * a.n_split + sp;

@@ -194,3 +194,68 @@ def test_quantisation_error_within_its_bound(kvc):
             assert err <= bound, (b, hq, err, bound)
             worst_rel = max(worst_rel, err / max(np.max(np.abs(ref[hq])), 1e-6))
     say(f"fp8 vs bf16 cache: worst error / max|out| = {worst_rel:.3e}")
+
+
+PF_CASES = [
+    (32, 8, 128, [0, 37, 300, 2000], [1, 17, 300, 200]),
+    (8, 2, 64, [5, 100], [70, 9]),
+    (16, 2, 64, [0, 3000], [130, 64]),
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,prefix,chunk", PF_CASES,
+                         ids=[f"{c[0]}/{c[1]}/{c[2]}" for c in PF_CASES])
+@pytest.mark.parametrize("split", [False, True])
+def test_chunked_prefill_over_fp8_cache(kvc, Hq, Hkv, D, prefix, chunk, split):
+    """Prefill chunks written into an fp8 cache (quantised as kv_append does)
+    and attended over the quantised prefix and chunk, against the oracle's
+    attention over the same dequantised rows."""
+    ctx = [p + c for p, c in zip(prefix, chunk)]
+    w = W.small_workload(f"fp8-pf-{Hq}-{D}", 580 + Hq + D, B=len(ctx), Hq=Hq, Hkv=Hkv, D=D,
+                         dtype="bf16", sigma=0.5)
+    nb = int(sum(W.blocks_for(c) for c in ctx)) + 3
+    bt = W.block_tables(w, np.array(ctx), nb)
+    vals = [W.sequence_values(w, b, n, n) for b, n in enumerate(ctx)]
+    kb = [_bf16(v[0]) for v in vals]
+    vb = [_bf16(v[1]) for v in vals]
+    qb = [_bf16(v[2]) for v in vals]
+    say(f"fp8 prefill {Hq}/{Hkv}/{D} split={split}: prefix {prefix}, chunk {chunk}")
+    cache = kvc.PagedKVCache.allocate(nb, Hkv, D, F8, fill_bits=FILL)
+    btd = torch.from_numpy(bt).cuda()
+    rows = [b for b in range(len(ctx)) if prefix[b] > 0]
+    if rows:
+        seq = np.concatenate([np.full(prefix[b], b, np.int32) for b in rows])
+        pos = np.concatenate([np.arange(prefix[b], dtype=np.int32) for b in rows])
+        s = kvc.slot_mapping(btd, nb, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(),
+                             err_flag=cache.err_flag)
+        kvc.kv_append(cache, s, _dev(np.concatenate([kb[b][:prefix[b]] for b in rows])),
+                      _dev(np.concatenate([vb[b][:prefix[b]] for b in rows])))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(chunk)]), dtype=torch.int32).cuda()
+    q = _dev(np.concatenate([qb[b][prefix[b]:] for b in range(len(ctx))]))
+    k = _dev(np.concatenate([kb[b][prefix[b]:] for b in range(len(ctx))]))
+    v = _dev(np.concatenate([vb[b][prefix[b]:] for b in range(len(ctx))]))
+    out = kvc.chunked_prefill_attention(cache, q, k, v, cu,
+                                        torch.tensor(prefix, dtype=torch.int32).cuda(), btd,
+                                        max(chunk), max_context_len=max(ctx) if split else None)
+    torch.cuda.synchronize()
+    assert int(cache.err_flag.item()) == 0
+    got = out.float().cpu().numpy()
+    scale = OA.default_scale(D)
+    kc = cache.k_cache.view(torch.uint8).cpu().numpy()
+    ksc = cache.k_scale.cpu().numpy()
+    off, worst = 0, 0.0
+    for b in range(len(ctx)):
+        codes, scales = OQ.quantize_rows(kb[b])
+        kq = OQ.dequantize_rows(codes, scales)
+        vq = OQ.dequantize_rows(*OQ.quantize_rows(vb[b]))
+        # the chunk's rows landed quantised, bit for bit
+        for p in sorted({prefix[b], ctx[b] - 1, prefix[b] + chunk[b] // 2}):
+            blk = bt[b, p // 16]
+            assert np.array_equal(kc[blk, :, p % 16, :], codes[p]), (b, p)
+            assert np.array_equal(ksc[blk, :, p % 16].view(np.uint32), scales[p].view(np.uint32))
+        for r in range(chunk[b]):
+            t = prefix[b] + r
+            ref = OA.attend_row(qb[b][t].astype(np.float64), kq[:t + 1], vq[:t + 1], scale)
+            worst = max(worst, assert_close(got[off + r], ref, "bf16", f"fp8 prefill {b} row {r}"))
+        off += chunk[b]
+    say(f"  max abs err {worst:.2e}")
