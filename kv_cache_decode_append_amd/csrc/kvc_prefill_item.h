@@ -45,6 +45,32 @@ constexpr int kRows = kPfWaves * kRowTiles * 16;    // 256 query rows per workgr
 constexpr int kKeyTile = 64;                        // keys per staged tile
 constexpr int kWaitVmcnt0 = 0x0F70;                 // s_waitcnt vmcnt(0) (expcnt, lgkmcnt: no wait)
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;      // bf16 (1, 1)
+constexpr uint32_t kDmaPastEnd = 0x7FFFFFF0u;        // buffer offset past any range: the load writes zeros
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Over each group of 16
+// lanes, lane i addresses 4 consecutive 16-bit elements A_i; lane j receives
+// A_{4k + j/4}[j % 4] for k = 0..3. Issued as inline assembly: the compiler
+// makes the builtin wait for every buffer->LDS load in flight, which would
+// drain the tile prefetch. The caller waits for the result with
+// tr_read_ready before using it.
+template <int OFF>
+__device__ __forceinline__ u32x2 tr_read_b64(uint32_t lds_addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "n"(OFF));
+  return r;
+}
+// Wait until at most `newer` pairs of transposing reads issued after (lo, hi)
+// are outstanding, i.e. until (lo, hi) have arrived; the register operands
+// order every use of the values after the wait.
+__device__ __forceinline__ void tr_read_ready(u32x2& lo, u32x2& hi, int newer) {
+  switch (newer) {
+    case 0: asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo), "+v"(hi)); break;
+    case 1: asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(lo), "+v"(hi)); break;
+    default: asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(lo), "+v"(hi)); break;
+  }
+}
 
 template <typename T> struct PfMfma;
 template <> struct PfMfma<bf16_tag> {
@@ -90,7 +116,13 @@ struct PfShape {
   static constexpr int VCH = BF16 ? 2 : 1;          // chunks per V unit
   static constexpr int K_LDS = kKeyTile * RB;
   static constexpr int V_LDS = BF16 ? D * VT_STRIDE * 2 : kKeyTile * RB;
-  static constexpr int TILES = 2 * K_LDS + 2 * V_LDS;   // two K and two V tile buffers
+  // bf16 tiles of 64 and 128 dims are staged by buffer->LDS loads into three
+  // K and three V buffers, both row-major with the chunk swizzle; the others
+  // go through registers into two K and two (transposed) V buffers
+  static constexpr bool DMA_OK = BF16 && NC >= 8;
+  static constexpr int TILES_REG = 2 * K_LDS + 2 * V_LDS;
+  static constexpr int TILES_DMA = DMA_OK ? 6 * K_LDS : 0;
+  static constexpr int TILES = TILES_REG > TILES_DMA ? TILES_REG : TILES_DMA;
   // pool rows of the blocks a workgroup reads, kept in LDS: 8,192 blocks
   // (131,072 keys) where the tile buffers leave room, else 2,048
   static constexpr int BT_CACHE = TILES <= 96 * 1024 ? 8192 : 2048;
@@ -152,6 +184,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
   using M = PfMfma<CT>;
   using Frag = typename M::Frag;
   constexpr int RB_MEM = F8 ? D : S::RB;              // bytes of one cached row
+  // bf16 caches of 64 / 128 dims: K and V tiles go from the pool straight
+  // into LDS (buffer->LDS loads), three tiles deep
+  constexpr bool DMA = S::DMA_OK && !F8;
   int32_t* bt_lds = reinterpret_cast<int32_t*>(smem + S::TILES);
   const int qt = work % a.n_qt;
   const int sp = (work / a.n_qt) % a.n_split;
@@ -281,6 +316,46 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
             ok ? (int64_t)r * 16 + (key & 15) : 0};
   };
   auto zero_unless = [](bool ok, const u32x4& v) { return ok ? v : u32x4{0u, 0u, 0u, 0u}; };
+
+  // Buffer->LDS staging: NC/8 loads of 1 KB per wave and tile for each of K
+  // and V. Load j of wave w fills rows (w + 8j) * 64/NC .. of the tile; lane l
+  // writes the 16-byte slot l % NC of row l / NC, so it fetches chunk
+  // (l % NC) ^ (key % NC) of that key (the swizzle every LDS reader expects).
+  constexpr int kDmaPerWave = DMA ? S::NC / 8 : 1;
+  constexpr int kKeysPerDma = 64 / S::NC;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  uint32_t dma_voff[kDmaPerWave];
+  int dma_key[kDmaPerWave];
+  // V fragment read offsets inside a tile, per dim tile (see v_frag)
+  int v_off[S::DT];
+  if constexpr (DMA) {
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) {
+      const int key = (wu + 8 * j) * kKeysPerDma + lane / S::NC;
+      dma_key[j] = key;
+      dma_voff[j] = (uint32_t)((key & 15) * S::RB + (((lane % S::NC) ^ (key % S::NC)) << 4));
+    }
+    const int v_row = 4 * g + (l16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+      v_off[dt] = v_row * S::RB + (((2 * dt + ((l16 & 3) >> 1)) ^ (v_row % S::NC)) << 4) + (l16 & 1) * 8;
+  }
+  // Tile kt of the pool (K or V) into LDS; keys past the sequence's and
+  // blocks that hold none read as zeros (the buffer range check).
+  auto dma_tile = [&](int kt, const uint8_t* pool, uint8_t* lds) {
+    const bool cached = 4 * (kt - t_begin) < S::BT_CACHE;
+    const bool edge = kt * kKeyTile + kKeyTile > kv_len;
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) {
+      const int inst = wu + 8 * j;
+      const int r = __builtin_amdgcn_readfirstlane(block_row(kt * 4 + inst * kKeysPerDma / 16, cached));
+      const uint8_t* base = pool + (r >= 0 ? (int64_t)r * (16 * S::RB) : 0);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, r >= 0 ? 16u * S::RB : 0u);
+      uint32_t voff = dma_voff[j];
+      if (edge && kt * kKeyTile + dma_key[j] >= kv_len) voff = kDmaPastEnd;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + inst * 1024), 16, voff, 0, 0, 0);
+    }
+  };
 
   // Register staging of K and V tiles. K runs two tiles ahead of V (QK^T of
   // tile k+1 is computed before PV of tile k), so each is loaded on its own.
@@ -496,25 +571,45 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
       l_run[n] = fmaf(l_run[n], alpha[n], rs);
     }
   };
+  // ---- V fragment (MFMA A operand of O^T += V^T . P^T) for key pair mp and
+  // dim tile dt: keys 32mp + 4g + 0..3 and 32mp + 16 + 4g + 0..3 of dim
+  // 16dt + l16, in the key order of the S^T accumulators. Issued as two
+  // 8-byte halves; v_frag_use waits for them (row-major tiles; `newer` =
+  // fragments issued after this one) and joins them.
+  struct VHalves { u32x2 lo, hi; };
+  auto v_frag_issue = [&](const uint8_t* v_lds, int mp, int dt) -> VHalves {
+    if constexpr (DMA) {
+      // row-major tile: each transposing read gathers 4 keys x 16 dims over a
+      // 16-lane group; lane i of the group addresses key 4g + i/4, dims
+      // 16dt + 4(i%4) .. +3 (chunk swizzle of that key's row applied)
+      // (the key offset is an immediate, so both key pairs share one address)
+      const uint32_t p = (uint32_t)(uintptr_t)(lds_void*)v_lds + (uint32_t)v_off[dt];
+      if (mp == 0) return {tr_read_b64<0>(p), tr_read_b64<16 * S::RB>(p)};
+      return {tr_read_b64<32 * S::RB>(p), tr_read_b64<48 * S::RB>(p)};
+    } else {
+      const uint16_t* rowp =
+          reinterpret_cast<const uint16_t*>(v_lds) + (dt * 16 + l16) * S::VT_STRIDE + mp * 32 + g * 4;
+      return {*reinterpret_cast<const u32x2*>(rowp), *reinterpret_cast<const u32x2*>(rowp + 16)};
+    }
+  };
+  auto v_frag_use = [&](VHalves& f, int newer) -> bf16x8_t {
+    if constexpr (DMA) tr_read_ready(f.lo, f.hi, newer);
+    return __builtin_bit_cast(bf16x8_t, u32x4{f.lo[0], f.lo[1], f.hi[0], f.hi[1]});
+  };
   // ---- O^T += V^T . P^T for one tile; V fragments are read one step ahead
   auto pv = [&](const uint8_t* v_lds, const PTile& pt) {
     if constexpr (S::BF16) {
-      const uint16_t* vt = reinterpret_cast<const uint16_t*>(v_lds);
-      auto load_vf = [&](int mp, int dt) -> Frag {
-        const uint16_t* rowp = vt + (dt * 16 + l16) * S::VT_STRIDE + mp * 32 + g * 4;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(rowp);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(rowp + 16);
-        return __builtin_bit_cast(bf16x8_t, u32x4{lo[0], lo[1], hi[0], hi[1]});
-      };
-      Frag vf[2];
-      vf[0] = load_vf(0, 0);
+      VHalves vf[2];
+      vf[0] = v_frag_issue(v_lds, 0, 0);
 #pragma unroll
       for (int st = 0; st < 2 * S::DT; ++st) {          // st = (mp, dt)
         const int mp = st / S::DT, dt = st % S::DT;
-        if (st + 1 < 2 * S::DT) vf[(st + 1) & 1] = load_vf((st + 1) / S::DT, (st + 1) % S::DT);
+        const bool more = st + 1 < 2 * S::DT;
+        if (more) vf[(st + 1) & 1] = v_frag_issue(v_lds, (st + 1) / S::DT, (st + 1) % S::DT);
+        const bf16x8_t a = v_frag_use(vf[st & 1], more ? 1 : 0);
 #pragma unroll
         for (int n = 0; n < kRowTiles; ++n)
-          o[n][dt] = M::mma(vf[st & 1], __builtin_bit_cast(bf16x8_t, pt.v[mp][n]), o[n][dt]);
+          o[n][dt] = M::mma(a, __builtin_bit_cast(bf16x8_t, pt.v[mp][n]), o[n][dt]);
       }
     } else {
 #pragma unroll
@@ -544,14 +639,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
     if constexpr (S::BF16) {
       constexpr int kSteps = 2 * S::DT, kAhead = 2;
       constexpr int kUnits = 3 + 16 * kRowTiles;
-      const uint16_t* vt = reinterpret_cast<const uint16_t*>(v_lds);
-      auto frag = [&](int st) {
-        const int mp = st / S::DT, dt = st % S::DT;
-        const uint16_t* rowp = vt + (dt * 16 + l16) * S::VT_STRIDE + mp * 32 + g * 4;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(rowp);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(rowp + 16);
-        return __builtin_bit_cast(bf16x8_t, u32x4{lo[0], lo[1], hi[0], hi[1]});
-      };
+      auto frag = [&](int st) { return v_frag_issue(v_lds, st / S::DT, st % S::DT); };
       float mx[kRowTiles], msafe[kRowTiles], rs[kRowTiles], pw[kRowTiles][4][4];
       auto unit = [&](int u) {
         if (u < kRowTiles) {
@@ -580,16 +668,18 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
           }
         }
       };
-      bf16x8_t vf[kAhead + 1];
+      VHalves vf[kAhead + 1];
   #pragma unroll
       for (int st = 0; st < kAhead; ++st) vf[st] = frag(st);
   #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
         if (st + kAhead < kSteps) vf[(st + kAhead) % (kAhead + 1)] = frag(st + kAhead);
         const int mp = st / S::DT, dt = st % S::DT;
+        const int newer = kSteps - 1 - st < kAhead ? kSteps - 1 - st : kAhead;
+        const bf16x8_t va = v_frag_use(vf[st % (kAhead + 1)], newer);
   #pragma unroll
         for (int n = 0; n < kRowTiles; ++n)
-          o[n][dt] = M::mma(vf[st % (kAhead + 1)], __builtin_bit_cast(bf16x8_t, pt.v[mp][n]), o[n][dt]);
+          o[n][dt] = M::mma(va, __builtin_bit_cast(bf16x8_t, pt.v[mp][n]), o[n][dt]);
   #pragma unroll
         for (int u = 0; u < kUnits; ++u)
           if (u * kSteps / kUnits == st) unit(u);
@@ -619,11 +709,73 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
   // are loaded during the iteration and stored behind it; K and V each have
   // two LDS buffers, and the barrier closing an iteration publishes the new
   // tiles after every wave has finished with the ones they overwrite.
-  auto kbuf = [&](int i) { return smem + (i & 1) * S::K_LDS; };
-  auto vbuf = [&](int i) { return smem + 2 * S::K_LDS + (i & 1) * S::V_LDS; };
   f32x4 sacc[4][kRowTiles];
   PTile pt;
   float alpha[kRowTiles];
+  // the next tile's weights and row sums are computed between the PV MFMAs;
+  // pin them there so they are not sunk past the rescale branch
+  auto pin = [&](PTile& pn) {
+#pragma unroll
+    for (int mp = 0; mp < 2; ++mp)
+#pragma unroll
+      for (int n = 0; n < kRowTiles; ++n) asm volatile("" : "+v"(pn.v[mp][n]));
+#pragma unroll
+    for (int n = 0; n < kRowTiles; ++n) asm volatile("" : "+v"(l_run[n]));
+  };
+  if constexpr (DMA) {
+    // Three K and three V buffers, tile t in buffer (t - t_begin) % 3.
+    // Iteration kt issues K(kt+3) and V(kt+2) into the buffers freed by the
+    // previous iteration, computes QK^T(kt+1) and PV(kt) + softmax(kt+1) as
+    // the register path does, then waits until K(kt+2) and V(kt+1) (issued
+    // one iteration earlier) have landed: every load has two iterations to
+    // arrive, and no tile passes through registers.
+    auto kb3 = [&](int b) { return smem + b * S::K_LDS; };
+    auto vb3 = [&](int b) { return smem + (3 + b) * S::K_LDS; };
+    // this wave's last `pending` loads may stay in flight; its LDS reads are done
+    auto wait_barrier = [](int pending) {
+      if (pending >= 4)
+        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (pending >= 2)
+        asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (pending >= 1)
+        asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    const bool has1 = t_begin + 1 < t_end, has2 = t_begin + 2 < t_end;
+    dma_tile(t_begin, kbase, kb3(0));
+    dma_tile(t_begin, vbase, vb3(0));
+    if (has1) {
+      dma_tile(t_begin + 1, kbase, kb3(1));
+      dma_tile(t_begin + 1, vbase, vb3(1));
+    }
+    if (has2) dma_tile(t_begin + 2, kbase, kb3(2));
+    // K(t_begin), V(t_begin), K(t_begin + 1) landed
+    wait_barrier((has1 ? kDmaPerWave : 0) + (has2 ? kDmaPerWave : 0));
+    qk(kb3(0), sacc);
+    mask(sacc, t_begin * kKeyTile);
+    softmax(sacc, pt, alpha);                         // o is still zero: no rescale
+    lds_barrier();                                     // K(t_begin) read by every wave
+    int b0 = 0;                                        // buffer of tile kt
+    for (int kt = t_begin; kt + 1 < t_end; ++kt) {
+      const int b1 = b0 == 2 ? 0 : b0 + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+      const bool k3 = kt + 3 < t_end, v2 = kt + 2 < t_end;
+      if (k3) dma_tile(kt + 3, kbase, kb3(b0));        // K(kt) was read last iteration
+      if (v2) dma_tile(kt + 2, vbase, vb3(b2));        // V(kt-1) likewise
+      qk(kb3(b1), sacc);
+      mask(sacc, (kt + 1) * kKeyTile);
+      PTile pt_next;
+      pv_softmax(vb3(b0), pt, sacc, pt_next, alpha);
+      pin(pt_next);
+      rescale(alpha);
+      pt = pt_next;
+      wait_barrier(((int)k3 + (int)v2) * kDmaPerWave);  // K(kt+2), V(kt+1) landed
+      b0 = b1;
+    }
+    pv(vb3(b0), pt);
+  } else {
+  auto kbuf = [&](int i) { return smem + (i & 1) * S::K_LDS; };
+  auto vbuf = [&](int i) { return smem + 2 * S::K_LDS + (i & 1) * S::V_LDS; };
   load_k(t_begin);
   load_v(t_begin);
   store_k(kbuf(t_begin));
@@ -646,14 +798,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
     PTile pt_next;
     if constexpr (S::BF16) {
       pv_softmax(vbuf(kt), pt, sacc, pt_next, alpha);
-      // the next tile's weights and row sums are computed between the PV
-      // MFMAs; pin them there so they are not sunk past the rescale branch
-#pragma unroll
-      for (int mp = 0; mp < 2; ++mp)
-#pragma unroll
-        for (int n = 0; n < kRowTiles; ++n) asm volatile("" : "+v"(pt_next.v[mp][n]));
-#pragma unroll
-      for (int n = 0; n < kRowTiles; ++n) asm volatile("" : "+v"(l_run[n]));
+      pin(pt_next);
     } else {
       pv(vbuf(kt), pt);
       softmax(sacc, pt_next, alpha);
@@ -665,6 +810,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
     lds_barrier();
   }
   pv(vbuf(t_end - 1), pt);
+  }
 
   if (bad) flag_error(a.err, bad);
 
