@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import workloads as W
-from tests.gpu_cases import PrefillCase, assert_close, device_bits, say
+from tests.gpu_cases import PrefillCase, assert_close, device_bits, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -156,3 +156,31 @@ def test_split_context_bound_too_small_is_flagged(kvc):
     case = PrefillCase(w, [3000], [7], 300)
     cache, _ = case.run_gpu(kvc, max_context_len=1000)
     assert int(cache.err_flag.item()) & kvc.DEVERR_CONTEXT
+
+
+@pytest.mark.parametrize("dtype,d,g", [("bf16", 128, 4), ("bf16", 64, 2), ("fp32", 64, 1)])
+def test_bad_prefix_block_id_is_flagged_not_faulted(kvc, dtype, d, g):
+    """A block id outside the pool in a prefix's table: the kernel reads no key
+    from it (zeros instead), flags the contract violation and writes finite rows.
+    Covers the buffer->LDS staging (bf16) and the register staging (fp32)."""
+    say(f"prefill with a bad prefix block id, {dtype} D={d} G={g}")
+    w = W.small_workload(f"pf-badblk-{dtype}", 987 + d + g, B=2, Hq=2 * g, Hkv=2, D=d, dtype=dtype,
+                         sigma=0.5 if dtype == "bf16" else 1.0)
+    case = PrefillCase(w, [100, 200], [40, 70], 64)
+    cache, _ = case.run_gpu(kvc)
+    assert int(cache.err_flag.item()) == 0
+    bad = case.bt.copy()
+    bad[1, 3] = case.num_blocks + 7                    # keys 48..63 of sequence 1's prefix
+    q = to_device(np.concatenate(case.q), w.dtype)
+    k = to_device(np.concatenate([case.k[i][case.prefix[i]:] for i in range(case.n)]), w.dtype)
+    v = to_device(np.concatenate([case.v[i][case.prefix[i]:] for i in range(case.n)]), w.dtype)
+    out = kvc.chunked_prefill_attention(
+        cache, q, k, v, torch.from_numpy(case.cu).cuda(),
+        torch.from_numpy(case.prefix.astype(np.int32)).cuda(), torch.from_numpy(bad).cuda(),
+        int(case.chunk.max()))
+    torch.cuda.synchronize()
+    assert int(cache.err_flag.item()) & kvc.DEVERR_BLOCK_ID
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    # sequence 0's table is intact: its rows are still right
+    assert_close(got[case.cu[0]:case.cu[1]], case.oracle_rows(0), dtype, "intact sequence 0")
