@@ -317,11 +317,13 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
   };
   auto zero_unless = [](bool ok, const u32x4& v) { return ok ? v : u32x4{0u, 0u, 0u, 0u}; };
 
-  // Buffer->LDS staging: NC/8 loads of 1 KB per wave and tile for each of K
-  // and V. Load j of wave w fills rows (w + 8j) * 64/NC .. of the tile; lane l
-  // writes the 16-byte slot l % NC of row l / NC, so it fetches chunk
-  // (l % NC) ^ (key % NC) of that key (the swizzle every LDS reader expects).
-  constexpr int kDmaPerWave = DMA ? S::NC / 8 : 1;
+  // Buffer->LDS staging: NC/W loads of 1 KB per wave and tile for each of K
+  // and V (W = kPfWaves). Load j of wave w fills rows (w + Wj) * 64/NC .. of
+  // the tile; lane l writes the 16-byte slot l % NC of row l / NC, so it
+  // fetches chunk (l % NC) ^ (key % NC) of that key (the swizzle every LDS
+  // reader expects).
+  static_assert(!DMA || S::NC % kPfWaves == 0, "whole 1 KB loads per wave");
+  constexpr int kDmaPerWave = DMA ? S::NC / kPfWaves : 1;
   constexpr int kKeysPerDma = 64 / S::NC;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   uint32_t dma_voff[kDmaPerWave];
@@ -331,7 +333,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
   if constexpr (DMA) {
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) {
-      const int key = (wu + 8 * j) * kKeysPerDma + lane / S::NC;
+      const int key = (wu + kPfWaves * j) * kKeysPerDma + lane / S::NC;
       dma_key[j] = key;
       dma_voff[j] = (uint32_t)((key & 15) * S::RB + (((lane % S::NC) ^ (key % S::NC)) << 4));
     }
@@ -347,7 +349,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
     const bool edge = kt * kKeyTile + kKeyTile > kv_len;
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) {
-      const int inst = wu + 8 * j;
+      const int inst = wu + kPfWaves * j;
       const int r = __builtin_amdgcn_readfirstlane(block_row(kt * 4 + inst * kKeysPerDma / 16, cached));
       const uint8_t* base = pool + (r >= 0 ? (int64_t)r * (16 * S::RB) : 0);
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, r >= 0 ? 16u * S::RB : 0u);
@@ -733,7 +735,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
     auto vb3 = [&](int b) { return smem + (3 + b) * S::K_LDS; };
     // this wave's last `pending` loads may stay in flight; its LDS reads are done
     auto wait_barrier = [](int pending) {
-      if (pending >= 4)
+      if (pending >= 8)
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (pending >= 4)
         asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       else if (pending >= 2)
         asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
