@@ -53,10 +53,9 @@
  *     accuracy cost and gives no scheme; this one keeps each appended row
  *     independent of the rows after it. Queries, new K/V and outputs are bf16.
  *     Supported by kvc_kv_append, kvc_paged_decode_attention,
- *     kvc_decode_append_attention and the chunked-prefill calls (which write
+ *     kvc_decode_append_attention, the chunked-prefill calls (which write
  *     the chunk quantised and dequantise tiles to bf16 as they stage them)
- *     with head_dim 64 or 128; kvc_mixed_step_attention returns
- *     KVC_ERR_UNSUPPORTED for such a cache.
+ *     and kvc_mixed_step_attention, with head_dim 64 or 128.
  */
 #ifndef KVC_H
 #define KVC_H
@@ -289,8 +288,11 @@ size_t kvc_mixed_workspace_bytes(int32_t n_decode, int32_t decode_max_context, i
  *              when a call starts: zero them once when the workspace is
  *              allocated; every call leaves them zero again. Calls that share
  *              a workspace must not overlap (same stream, or ordered).
- * Supported: bf16 caches with head_dim 64 or 128 and fp32 caches with head_dim
- * 32, G = Hq / num_kv_heads in {1, 2, 4}; KVC_ERR_UNSUPPORTED otherwise.
+ * Supported: bf16 and fp8 caches with head_dim 64 or 128 and fp32 caches with
+ * head_dim 32, G = Hq / num_kv_heads in {1, 2, 4}; KVC_ERR_UNSUPPORTED
+ * otherwise. With an fp8 cache the new decode rows and the chunks are written
+ * quantised (the codes and scales kvc_kv_append and the chunked-prefill calls
+ * write), and q, k_new, v_new, the chunks' K/V and the outputs are bf16.
  * Returns KVC_ERR_WORKSPACE for a missing or short workspace and validates
  * like the two calls it replaces. */
 int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_batch* batch, int32_t Hq,

@@ -42,4 +42,43 @@ __device__ __forceinline__ int chunk_append_one(uint8_t* kc, uint8_t* vc, const 
   return 0;
 }
 
+// fp8 cache: the 8 values of chunk c of kv head h of row r (packed bf16 k/v,
+// rows from t0, positions from p0, as chunk_append_one), coded with their
+// row's scale: amax / 448 over the row, codes = E4M3(x * 448 / amax), a row
+// below kZeroRowAmax stored as zeros with scale 0. The NCB = head_dim / 8
+// lanes of one row must form an aligned group of 8 or 16 lanes and all call
+// this together (the amax is a reduction over the group); a lane whose `in`
+// is false only takes part in the reduction. Returns the error bit as
+// chunk_append_one does (nothing written for that row).
+template <int NCB>
+__device__ __forceinline__ int chunk_append_fp8_one(uint8_t* kc, uint8_t* vc, float* ks, float* vs,
+                                                    const uint8_t* k, const uint8_t* v,
+                                                    const int32_t* bt_row, int32_t max_blocks,
+                                                    int32_t num_blocks, int32_t hkv, int32_t t0,
+                                                    int32_t p0, int32_t r, int32_t h, int32_t c,
+                                                    bool in) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int64_t src = (((int64_t)(t0 + r) * hkv + h) * NCB + c) * 16;
+  const u32x4 kx = in ? *reinterpret_cast<const u32x4*>(k + src) : zero;
+  const u32x4 vx = in ? *reinterpret_cast<const u32x4*>(v + src) : zero;
+  const float ka = group_max<NCB>(bf16x8_amax(kx));
+  const float va = group_max<NCB>(bf16x8_amax(vx));
+  if (!in) return 0;
+  const int32_t p = p0 + r, lb = p >> 4;
+  if (lb >= max_blocks) return KVC_DEVERR_CONTEXT;
+  const int32_t blk = bt_row[lb];
+  if (blk < 0 || blk >= num_blocks) return KVC_DEVERR_BLOCK_ID;
+  const int64_t prow = ((int64_t)blk * hkv + h) * 16 + (p & 15);
+  const bool kz = !(ka >= kZeroRowAmax), vz = !(va >= kZeroRowAmax);
+  *reinterpret_cast<u32x2*>(kc + prow * (NCB * 8) + c * 8) =
+      kz ? u32x2{0u, 0u} : bf16x8_to_e4m3x8(kx, kE4M3Max / ka);
+  *reinterpret_cast<u32x2*>(vc + prow * (NCB * 8) + c * 8) =
+      vz ? u32x2{0u, 0u} : bf16x8_to_e4m3x8(vx, kE4M3Max / va);
+  if (c == 0) {
+    ks[prow] = kz ? 0.f : ka / kE4M3Max;
+    vs[prow] = vz ? 0.f : va / kE4M3Max;
+  }
+  return 0;
+}
+
 }  // namespace kvc

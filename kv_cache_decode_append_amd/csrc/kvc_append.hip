@@ -154,38 +154,15 @@ __global__ __launch_bounds__(256) void chunk_append_fp8_kernel(
   const int32_t c = (int32_t)(i % NCB);
   const int32_t r = (int32_t)(row / hkv);
   const int32_t h = (int32_t)(row - (int64_t)r * hkv);
-  const bool in = ok && r < C;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  const int64_t src = (((int64_t)(t0 + r) * hkv + h) * NCB + c) * 16;
-  const u32x4 kx = in ? *reinterpret_cast<const u32x4*>(k + src) : zero;
-  const u32x4 vx = in ? *reinterpret_cast<const u32x4*>(v + src) : zero;
-  const float ka = group_max<NCB>(bf16x8_amax(kx));
-  const float va = group_max<NCB>(bf16x8_amax(vx));
+  // every lane of a row's group takes part in its reduction: no early exit
+  const int bad = chunk_append_fp8_one<NCB>(kc, vc, ks, vs, k, v,
+                                            block_table + (int64_t)s * max_blocks, max_blocks,
+                                            num_blocks, hkv, t0, p0, r, h, c, ok && r < C);
   if (!ok) {
     if (i == 0) flag_error(err, KVC_DEVERR_CONTEXT);
     return;
   }
-  if (!in) return;
-  const int32_t p = p0 + r, lb = p >> 4;
-  if (lb >= max_blocks) {
-    if (h == 0 && c == 0) flag_error(err, KVC_DEVERR_CONTEXT);
-    return;
-  }
-  const int32_t blk = block_table[(int64_t)s * max_blocks + lb];
-  if (blk < 0 || blk >= num_blocks) {
-    if (h == 0 && c == 0) flag_error(err, KVC_DEVERR_BLOCK_ID);
-    return;
-  }
-  const int64_t prow = ((int64_t)blk * hkv + h) * 16 + (p & 15);
-  const bool kz = !(ka >= kZeroRowAmax), vz = !(va >= kZeroRowAmax);
-  *reinterpret_cast<u32x2*>(kc + prow * (NCB * 8) + c * 8) =
-      kz ? u32x2{0u, 0u} : bf16x8_to_e4m3x8(kx, kE4M3Max / ka);
-  *reinterpret_cast<u32x2*>(vc + prow * (NCB * 8) + c * 8) =
-      vz ? u32x2{0u, 0u} : bf16x8_to_e4m3x8(vx, kE4M3Max / va);
-  if (c == 0) {
-    ks[prow] = kz ? 0.f : ka / kE4M3Max;
-    vs[prow] = vz ? 0.f : va / kE4M3Max;
-  }
+  if (bad && h == 0 && c == 0) flag_error(err, bad);
 }
 
 int launch_chunk_append(const kvc_cache* c, const void* k, const void* v, int32_t n_seqs,

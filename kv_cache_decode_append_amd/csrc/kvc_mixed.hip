@@ -65,7 +65,7 @@ struct MixedArgs {
   const uint8_t* k_new; // the decode rows' new K/V, [n_dec][hkv][D]
   const uint8_t* v_new;
   int32_t plan;         // 1: phase-0 item 0 orders the decode rows
-  int32_t nc;           // 16-byte chunks per K/V row
+  int32_t nc;           // 16-byte chunks per new K/V row (bf16 rows for an fp8 cache)
   MixedHeader* hdr;
   int32_t* dec_order;   // [n_dec]: decode rows, longest first (when planned)
   int32_t n_dec;
@@ -111,15 +111,23 @@ __device__ __forceinline__ void plan_decode(const MixedArgs& m, int32_t* scratch
 
 // The new K/V of decode row b for kv head kvh at position context_len - 1,
 // written by the decode item itself before it reads the row (a workgroup
-// barrier orders the two). A row with an empty context holds no token.
+// barrier orders the two); an fp8 cache gets the row's codes and scale, made
+// by the first D / 8 lanes together. A row with an empty context holds no token.
+template <typename T, int D>
 __device__ __forceinline__ void append_decode_row(const MixedArgs& m, int b, int kvh, int tid) {
   const DecodeArgs& a = m.dec;
   if (tid < m.nc) {
     const int ctx = effective_ctx(a, b, false);
     if (ctx >= 1) {
-      const int bad = chunk_append_one((uint8_t*)a.kc, (uint8_t*)a.vc, m.k_new, m.v_new,
-                                       a.bt + (size_t)b * a.max_blocks, a.max_blocks,
-                                       a.num_blocks, a.hkv, m.nc, b, ctx - 1, 0, kvh, tid);
+      const int32_t* bt_row = a.bt + (size_t)b * a.max_blocks;
+      int bad;
+      if constexpr (std::is_same_v<T, fp8_tag>)
+        bad = chunk_append_fp8_one<D / 8>((uint8_t*)a.kc, (uint8_t*)a.vc, a.ks, a.vs, m.k_new,
+                                          m.v_new, bt_row, a.max_blocks, a.num_blocks, a.hkv, b,
+                                          ctx - 1, 0, kvh, tid, true);
+      else
+        bad = chunk_append_one((uint8_t*)a.kc, (uint8_t*)a.vc, m.k_new, m.v_new, bt_row,
+                               a.max_blocks, a.num_blocks, a.hkv, m.nc, b, ctx - 1, 0, kvh, tid);
       if (bad && tid == 0) flag_error(a.err, bad);
     }
   }
@@ -127,7 +135,10 @@ __device__ __forceinline__ void append_decode_row(const MixedArgs& m, int b, int
   __syncthreads();
 }
 
-// Phase 0: rows [64 * slice, 64 * slice + 64) of prefill chunk s.
+// Phase 0: rows [64 * slice, 64 * slice + 64) of prefill chunk s (coded with
+// their row scales for an fp8 cache: a row's D / 8 chunks are consecutive
+// indices, so they sit in one aligned lane group of every pass).
+template <typename T, int D>
 __device__ __forceinline__ void append_slice(const MixedArgs& m, int idx) {
   const PrefillArgs& p = m.pf;
   const int s = idx / m.n_slices, slice = idx % m.n_slices;
@@ -139,8 +150,14 @@ __device__ __forceinline__ void append_slice(const MixedArgs& m, int idx) {
   int bad = 0;
   for (int i = threadIdx.x; i < (r1 - r0) * per_row; i += kMixThreads) {
     const int r = r0 + i / per_row, hc = i % per_row;
-    bad |= chunk_append_one((uint8_t*)p.kc, (uint8_t*)p.vc, m.k_pf, m.v_pf, bt_row, p.max_blocks,
-                            p.num_blocks, p.hkv, m.nc, t0, p0, r, hc / m.nc, hc % m.nc);
+    if constexpr (std::is_same_v<T, fp8_tag>)
+      bad |= chunk_append_fp8_one<D / 8>((uint8_t*)p.kc, (uint8_t*)p.vc, const_cast<float*>(p.ks),
+                                         const_cast<float*>(p.vs), m.k_pf, m.v_pf, bt_row,
+                                         p.max_blocks, p.num_blocks, p.hkv, t0, p0, r, hc / m.nc,
+                                         hc % m.nc, true);
+    else
+      bad |= chunk_append_one((uint8_t*)p.kc, (uint8_t*)p.vc, m.k_pf, m.v_pf, bt_row, p.max_blocks,
+                              p.num_blocks, p.hkv, m.nc, t0, p0, r, hc / m.nc, hc % m.nc);
   }
   if (bad) flag_error(p.err, bad);
 }
@@ -158,8 +175,8 @@ __device__ __forceinline__ const MixedArgs* fresh_args() {
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kMixThreads) void mixed_step_kernel(MixedArgs) {
-  using DS = DecodeShape<T, D, G, kMixWaves>;
-  using PS = PfShape<T, D, G>;
+  using DS = DecodeShape<ComputeT<T>, D, G, kMixWaves>;
+  using PS = PfShape<PfComputeT<T>, D, G>;
   constexpr int WORK = DS::SMEM > PS::SMEM ? DS::SMEM : PS::SMEM;
   __shared__ __attribute__((aligned(16))) uint8_t smem[WORK + kMixMaxDecode * 4 + 64];
   int32_t* order_lds = reinterpret_cast<int32_t*>(smem + WORK);
@@ -181,7 +198,7 @@ __global__ __launch_bounds__(kMixThreads) void mixed_step_kernel(MixedArgs) {
       if (m.plan && item == 0)
         plan_decode(m, reinterpret_cast<int32_t*>(smem));
       else
-        append_slice(m, item - m.plan);
+        append_slice<T, D>(m, item - m.plan);
       __threadfence();                             // publish this item's writes
       __syncthreads();
       if (tid == 0) atomicAdd(&m.hdr->phase0_done, 1);
@@ -233,7 +250,7 @@ __global__ __launch_bounds__(kMixThreads) void mixed_step_kernel(MixedArgs) {
       } else {
         const MixedArgs& mi = *fresh_args();
         const int b = mi.plan ? order_lds[idx / hkv] : idx / hkv, kvh = idx % hkv;
-        append_decode_row(mi, b, kvh, my_tid);
+        append_decode_row<T, D>(mi, b, kvh, my_tid);
         decode_item<T, D, G, kMixWaves, true, false>(mi.dec, kvh, b, 0, smem, my_tid);
       }
     }
@@ -294,8 +311,8 @@ int launch_mixed(const MixedArgs& m, int64_t n_items_max, hipStream_t st) {
 }
 
 // Instantiated where both item bodies fit the 256 registers a lane has at 8
-// waves per workgroup without spilling: bf16 head_dim 64 and 128, fp32
-// head_dim 32, with G <= 4.
+// waves per workgroup without spilling: bf16 and fp8 head_dim 64 and 128,
+// fp32 head_dim 32, with G <= 4.
 template <typename T, int D>
 int mixed_g(const MixedArgs& m, int G, int64_t n, hipStream_t st) {
   switch (G) {
@@ -310,6 +327,9 @@ int dispatch_mixed(const MixedArgs& m, int dtype, int D, int G, int64_t n, hipSt
   if (dtype == KVC_BF16) {
     if (D == 64) return mixed_g<bf16_tag, 64>(m, G, n, st);
     if (D == 128) return mixed_g<bf16_tag, 128>(m, G, n, st);
+  } else if (dtype == KVC_FP8) {
+    if (D == 64) return mixed_g<fp8_tag, 64>(m, G, n, st);
+    if (D == 128) return mixed_g<fp8_tag, 128>(m, G, n, st);
   } else if (D == 32) {
     return mixed_g<float, 32>(m, G, n, st);
   }
@@ -317,7 +337,7 @@ int dispatch_mixed(const MixedArgs& m, int dtype, int D, int G, int64_t n, hipSt
 }
 
 bool mixed_supported(int dtype, int D, int G) {
-  const bool dim_ok = dtype == KVC_BF16 ? (D == 64 || D == 128) : D == 32;
+  const bool dim_ok = dtype == KVC_F32 ? D == 32 : (D == 64 || D == 128);
   return dim_ok && (G == 1 || G == 2 || G == 4);
 }
 
@@ -337,7 +357,6 @@ extern "C" int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_
   using namespace kvc;
   int st = check_cache(cache);
   if (st != KVC_OK) return st;
-  if (cache->dtype == KVC_FP8) return KVC_ERR_UNSUPPORTED;
   if (!bt) return KVC_ERR_NULL;
   if (Hq <= 0 || Hq % cache->num_kv_heads != 0) return KVC_ERR_SHAPE;
   const int hkv = cache->num_kv_heads, D = cache->head_dim, G = Hq / hkv;
@@ -384,8 +403,8 @@ extern "C" int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_
   a.max_blocks = b.decode_max_blocks;
   a.max_ctx = b.decode_max_context;
   a.part_blocks = 1 << 30;
-  a.ks = nullptr;
-  a.vs = nullptr;
+  a.ks = cache->k_scale;      // fp8 row scales (null otherwise)
+  a.vs = cache->v_scale;
   a.n_part = 1;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
 
@@ -411,8 +430,8 @@ extern "C" int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_
   p.scale_log2 = a.scale_log2;
   p.ws_o = nullptr;
   p.ws_ml = nullptr;
-  p.ks = nullptr;
-  p.vs = nullptr;
+  p.ks = cache->k_scale;
+  p.vs = cache->v_scale;
 
   m.k_pf = reinterpret_cast<const uint8_t*>(b.k_prefill);
   m.v_pf = reinterpret_cast<const uint8_t*>(b.v_prefill);
@@ -421,7 +440,8 @@ extern "C" int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_
   // order the decode rows only when there are many more decode items than
   // workgroups and some row is long enough for its order to matter
   m.plan = (int64_t)n_dec * hkv > 2 * 256 && b.decode_max_context > 4096 ? 1 : 0;
-  m.nc = D * dtype_bytes(cache->dtype) / 16;
+  // 16-byte chunks of a new K/V row as passed in (bf16 rows for an fp8 cache)
+  m.nc = D * (cache->dtype == KVC_FP8 ? 2 : dtype_bytes(cache->dtype)) / 16;
   m.hdr = reinterpret_cast<MixedHeader*>(ws);
   m.dec_order = reinterpret_cast<int32_t*>(ws + 256);
   m.n_dec = n_dec;

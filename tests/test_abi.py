@@ -185,6 +185,9 @@ def test_fp8_cache_rules():
     c = _cache(dtype=2, head_dim=64, k_scale=1, v_scale=1)
     byref = ctypes.byref(c)
     assert LIB.kvc_kv_append(byref, 1, 1, 1, 0, None) == 0
-    # the mixed step does not take an fp8 cache
-    assert LIB.kvc_mixed_step_attention(byref, ctypes.byref(_mixed()), 1, 0.1, 1, 256, None) == -4
+    # the mixed step takes an fp8 cache of head_dim 64 or 128 (here: nothing to do)
+    assert LIB.kvc_mixed_step_attention(byref, ctypes.byref(_mixed()), 4, 0.1, 1, 256, None) == 0
+    c32 = _cache(dtype=2, head_dim=32, k_scale=1, v_scale=1)
+    assert LIB.kvc_mixed_step_attention(ctypes.byref(c32), ctypes.byref(_mixed()), 4, 0.1, 1, 256,
+                                        None) == -4
     assert kvc.KVC_FP8 == 2

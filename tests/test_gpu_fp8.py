@@ -259,3 +259,80 @@ def test_chunked_prefill_over_fp8_cache(kvc, Hq, Hkv, D, prefix, chunk, split):
             worst = max(worst, assert_close(got[off + r], ref, "bf16", f"fp8 prefill {b} row {r}"))
         off += chunk[b]
     say(f"  max abs err {worst:.2e}")
+
+
+_LONG = np.random.default_rng(5911).integers(1, 6000, 80).tolist()
+MIXED_CASES = [
+    (32, 8, 128, [1, 2, 17, 300, 2000, 5000], [0, 100, 3000], [33, 200, 64]),
+    (16, 8, 128, [16, 33, 1000], [37], [300]),
+    (8, 2, 64, [1, 65, 2500], [0, 250], [130, 17]),
+    (32, 8, 128, _LONG, [2000], [300]),          # 640 decode items: rows ordered longest first
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dec_ctx,pf_prefix,pf_chunk", MIXED_CASES,
+                         ids=["4-heads-mix", "g2", "d64", "80-rows"])
+def test_mixed_step_over_fp8_cache(kvc, Hq, Hkv, D, dec_ctx, pf_prefix, pf_chunk):
+    """The one-launch mixed step over an fp8 cache against the same step as
+    separate calls (fused append + decode, then chunk write + prefill): the
+    codes and scales it writes bit for bit, the prefill rows bit for bit (the
+    same work item), and every decode row and sampled prefill rows against the
+    oracle's attention over the dequantised rows, with the bf16 tolerance."""
+    from tests.test_gpu_mixed import MixedCase
+    case = MixedCase(f"fp8-mixed-{Hq}-{D}-{len(dec_ctx)}", 590 + Hq + D + len(dec_ctx), Hq, Hkv, D,
+                     "bf16", dec_ctx, pf_prefix, pf_chunk)
+    say(f"fp8 mixed step {Hq}/{Hkv}/{D}: {case.n_dec} decode rows, chunks {pf_chunk}")
+
+    def fp8_fill():
+        cache = kvc.PagedKVCache.allocate(case.nb, Hkv, D, F8, fill_bits=FILL)
+        btd = torch.from_numpy(case.bt).cuda()
+        rows = [b for b in range(len(case.ctx)) if case.cached_len(b) > 0]
+        seq = np.concatenate([np.full(case.cached_len(b), b, np.int32) for b in rows])
+        pos = np.concatenate([np.arange(case.cached_len(b), dtype=np.int32) for b in rows])
+        s = kvc.slot_mapping(btd, case.nb, torch.from_numpy(seq).cuda(),
+                             torch.from_numpy(pos).cuda(), err_flag=cache.err_flag)
+        cached = lambda i: np.concatenate([case.vals[b][i][:case.cached_len(b)] for b in rows])
+        kvc.kv_append(cache, s, _dev(cached(0)), _dev(cached(1)))
+        return cache
+
+    one, two = fp8_fill(), fp8_fill()
+    inp = case.inputs()
+    out_dec, out_pf = kvc.mixed_step_attention(one, Hq, **inp)
+    ref_dec = kvc.decode_append_attention(two, inp["q_decode"], inp["k_new"], inp["v_new"],
+                                          inp["decode_block_table"], inp["decode_context_lens"],
+                                          inp["decode_max_context"])
+    ref_pf = kvc.chunked_prefill_attention(two, inp["q_prefill"], inp["k_prefill"],
+                                           inp["v_prefill"], inp["cu_chunk_lens"],
+                                           inp["prefix_lens"], inp["prefill_block_table"],
+                                           inp["prefill_max_chunk"])
+    torch.cuda.synchronize()
+    assert int(one.err_flag.item()) == 0 and int(two.err_flag.item()) == 0
+    for x, y in ((one.k_cache, two.k_cache), (one.v_cache, two.v_cache)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    for x, y in ((one.k_scale, two.k_scale), (one.v_scale, two.v_scale)):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+    assert torch.equal(out_pf.view(torch.int16), ref_pf.view(torch.int16))
+
+    scale = OA.default_scale(D)
+    deq = lambda x: OQ.dequantize_rows(*OQ.quantize_rows(_bf16(x)))
+    worst = 0.0
+    got = out_dec.float().cpu().numpy()
+    ref2 = ref_dec.float().cpu().numpy()
+    for b in range(case.n_dec):
+        c = case.dec_ctx[b]
+        k, v, q = case.vals[b]
+        ref = OA.attend_row(_bf16(q[c - 1]).astype(np.float64), deq(k[:c]), deq(v[:c]), scale)
+        worst = max(worst, assert_close(got[b], ref, "bf16", f"fp8 mixed decode row {b} ctx {c}"))
+        assert_close(got[b], ref2[b].astype(np.float64), "bf16", f"fp8 mixed vs separate, row {b}")
+    got = out_pf.float().cpu().numpy()
+    off = 0
+    for i, (p0, C) in enumerate(zip(pf_prefix, pf_chunk)):
+        k, v, q = case.vals[case.n_dec + i]
+        kq, vq = deq(k[:p0 + C]), deq(v[:p0 + C])
+        for r in sorted({0, C // 3, C - 1}):
+            t = p0 + r
+            ref = OA.attend_row(_bf16(q[t]).astype(np.float64), kq[:t + 1], vq[:t + 1], scale)
+            worst = max(worst, assert_close(got[off + r], ref, "bf16",
+                                            f"fp8 mixed chunk {i} row {r}"))
+        off += C
+    say(f"  max abs err {worst:.2e}")
