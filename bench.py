@@ -11,7 +11,8 @@ attention (split-K merge pass only when a sequence spans several partitions).
 Inputs are synthetic and resident in HBM before the timed region.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--workload c3-decode|c5-decode|c5-prefill]
+                    [--workload c3-decode|c3-fp8|c4-mixed|c4-mixed-fp8|c5-decode|
+                                c5-prefill|c5-prefill-fp8|prefix-warm|queue-replay]
 
 The default workload is the one above (c3-decode). c5-decode (8 sequences at
 32,000 tokens, split-K) and c5-prefill (8 x a 2,048-token chunk over a
@@ -47,7 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--workload", default="c3-decode",
-                    choices=["c3-decode", "c3-fp8", "c4-mixed", "c5-decode", "c5-prefill",
+                    choices=["c3-decode", "c3-fp8", "c4-mixed", "c4-mixed-fp8", "c5-decode",
+                             "c5-prefill",
                              "c5-prefill-fp8", "prefix-warm", "queue-replay"])
     ap.add_argument("--direct-steps", type=int, default=400,
                     help="queue-replay: leading steps of each continuous plan run for real")
@@ -159,6 +161,8 @@ def main():
         return bench_prefix_warm(args)
     if args.workload == "c4-mixed":
         return bench_c4_mixed(args)
+    if args.workload == "c4-mixed-fp8":
+        return bench_c4_mixed(args, fp8=True)
     if args.workload == "queue-replay":
         return bench_queue_replay(args)
     if args.workload == "c3-fp8":
@@ -481,14 +485,16 @@ def bench_c5_prefill(args, fp8=False):
     print(json.dumps(res), flush=True)
 
 
-def bench_c4_mixed(args):
+def bench_c4_mixed(args, fp8=False):
     """The skewed continuous-batching step: 210 sequences with lognormal context
     lengths (median 6,000, tail clipped at 32,000); 206 decode one token each
     (one fused append + attention launch, split over partitions for the long
     ones) and 4 run a 2,048-token prefill chunk over their prefix (one launch).
     The same step is also timed as ONE launch of the mixed-batch kernel. One
     layer's pool (~6.5 GB, far larger than the caches) is timed per step and
-    reported per layer and for 32 layers."""
+    reported per layer and for 32 layers. With fp8 the cache holds E4M3 codes
+    and one fp32 scale per (token, kv head) row for K and for V; the decode
+    bytes count both."""
     import torch
 
     import kv_cache_decode_append_amd as kvc
@@ -503,9 +509,13 @@ def bench_c4_mixed(args):
     need = int(sum(W.blocks_for(int(c)) for c in ctx))
     nb = need + need // 100
     bt_all = torch.from_numpy(W.block_tables(w, ctx, nb)).to(dev)
-    cache = kvc.PagedKVCache.allocate(nb, Hkv, D, torch.bfloat16, device=dev)
-    cache.k_cache.normal_(0, 0.5)
-    cache.v_cache.normal_(0, 0.5)
+    if fp8:
+        cache = kvc.PagedKVCache.allocate(nb, Hkv, D, torch.float8_e4m3fn, device=dev)
+        fill_fp8_pools(cache)
+    else:
+        cache = kvc.PagedKVCache.allocate(nb, Hkv, D, torch.bfloat16, device=dev)
+        cache.k_cache.normal_(0, 0.5)
+        cache.v_cache.normal_(0, 0.5)
     nd, chunk = len(dec_rows), W.C4_CHUNK
     q_dec = torch.empty(nd, Hq, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
     k_dec = torch.empty(nd, Hkv, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5)
@@ -569,16 +579,20 @@ def bench_c4_mixed(args):
     ms_one_pre = _timed(one_launch_pre, max(1, args.steps // 4), max(1, args.warmup // 4))
     assert int(cache.err_flag.item()) == 0
     assert int(mws[:256].count_nonzero().item()) == 0
-    kv_dec = int(ctx[dec_rows].sum()) * Hkv * D * 2 * 2
+    # K and V per token and kv head: bf16 values, or fp8 codes plus two fp32 row scales
+    kv_dec = int(ctx[dec_rows].sum()) * Hkv * ((D + 4) * 2 if fp8 else D * 2 * 2)
     pairs = sum(Hq * (chunk * (int(c) - chunk) + chunk * (chunk + 1) // 2) for c in ctx[pre_rows])
     flop = pairs * 4 * D
     gbs = kv_dec / (ms_dec * 1e-3) / 1e9
     tf = flop / (ms_pre * 1e-3) / 1e12
     res = _base_line(args, "skewed mixed step (206 decode rows + 4 prefill chunks): decode KV-read "
-                     "GB/s", round(gbs, 1), "GB/s", ms_step, "bf16",
+                     "GB/s" + (", fp8 E4M3 cache" if fp8 else ""), round(gbs, 1), "GB/s", ms_step,
+                     "fp8-e4m3 cache, bf16 compute" if fp8 else "bf16",
                      {"workload": "210 sequences, lognormal context (median 6,000, clipped at "
                                   "32,000), 206 decode + 4 x 2,048-token prefill chunks, GQA "
-                                  "32/8, head_dim 128, bf16, one layer timed",
+                                  "32/8, head_dim 128, "
+                                  + ("fp8 E4M3 cache with row scales" if fp8 else "bf16")
+                                  + ", one layer timed",
                       "B": int(w.B), "ctx_sum": int(ctx.sum()), "ctx_max": int(ctx.max()),
                       "prefill_rows": pre_rows.tolist(), "pool_blocks": nb},
                      {"bound": "hbm", "kernel": "paged_decode_kernel + decode_merge_kernel",
