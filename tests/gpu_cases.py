@@ -118,9 +118,11 @@ class DecodeCase:
         return seq, pos
 
     # ---------------------------------------------------------------- GPU side
-    def run_gpu(self, kvc, max_context_len: int | None = None):
+    def run_gpu(self, kvc, max_context_len: int | None = None, fused: bool = False):
         """Fill the cache through slot_mapping + kv_append (cached tokens, then
-        the new ones), then decode. Returns (cache, out, slots_all)."""
+        the new ones), then decode; with `fused` the new tokens are appended by
+        the decode launch itself (decode_append_attention, the launch the
+        benchmark times). Returns (cache, out)."""
         w, dev = self.w, "cuda"
         cache = kvc.PagedKVCache.allocate(self.num_blocks, w.Hkv, w.D, TDTYPE[w.dtype],
                                           fill_bits=FILL)
@@ -136,6 +138,16 @@ class DecodeCase:
             s_old = kvc.slot_mapping(bt, self.num_blocks, seq, pos, err_flag=cache.err_flag)
             kvc.kv_append(cache, s_old, kk, vv)
         live = [b for b in range(self.B) if self.ctx[b] > 0]
+        if fused:
+            assert len(live) == self.B, "the fused launch appends one token to every row"
+            q = to_device(self.q, w.dtype)
+            kn = to_device(np.stack([self.k[b][-1] for b in live]), w.dtype)
+            vn = to_device(np.stack([self.v[b][-1] for b in live]), w.dtype)
+            ctx = torch.from_numpy(self.ctx.astype(np.int32)).to(dev)
+            mcl = int(self.ctx.max()) if max_context_len is None else max_context_len
+            out = kvc.decode_append_attention(cache, q, kn, vn, bt, ctx, mcl)
+            torch.cuda.synchronize()
+            return cache, out
         if live:
             seq = torch.tensor(live, dtype=torch.int32, device=dev)
             pos = torch.tensor([int(self.ctx[b]) - 1 for b in live], dtype=torch.int32, device=dev)

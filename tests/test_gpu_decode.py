@@ -23,8 +23,8 @@ def kvc():
     return m
 
 
-def _check_case(kvc, case: DecodeCase, check_pool=True, what=""):
-    cache, out = case.run_gpu(kvc)
+def _check_case(kvc, case: DecodeCase, check_pool=True, what="", fused=False):
+    cache, out = case.run_gpu(kvc, fused=fused)
     assert int(cache.err_flag.item()) == 0
     if check_pool:
         pk, pv = case.oracle_pool()
@@ -105,6 +105,22 @@ def test_c3_full_layer_bf16(kvc):
     ctx = W.context_lengths(W.C3)
     case = DecodeCase(W.C3, ctx, W.C3_POOL_BLOCKS)
     _check_case(kvc, case, what="C3")
+
+
+def test_c3_full_layer_bf16_fused(kvc):
+    """The launch bench.py times: one fused append + decode per layer at C3."""
+    say("C3 full layer bf16, fused append + decode launch")
+    ctx = W.context_lengths(W.C3)
+    case = DecodeCase(W.C3, ctx, W.C3_POOL_BLOCKS)
+    _check_case(kvc, case, what="C3 fused", fused=True)
+
+
+def test_c5_long_decode_fused(kvc):
+    """C5 decode as its bench line times it: fused append + split-K decode + merge."""
+    say("C5 decode: B=8, ctx 32,000, bf16, fused append + split-K")
+    ctx = W.context_lengths(W.C5)
+    case = DecodeCase(W.C5, ctx, 8 * W.blocks_for(W.C5_CTX))
+    _check_case(kvc, case, check_pool=False, what="C5 decode fused", fused=True)
 
 
 def test_c3_shape_fp32_cache(kvc):

@@ -336,3 +336,52 @@ def test_mixed_step_over_fp8_cache(kvc, Hq, Hkv, D, dec_ctx, pf_prefix, pf_chunk
                                             f"fp8 mixed chunk {i} row {r}"))
         off += C
     say(f"  max abs err {worst:.2e}")
+
+
+def test_c3_full_size_fused_fp8(kvc):
+    """The launch the fp8 bench line times, at its full size: the C3 batch (64
+    sequences, contexts 2,000..2,300, GQA 32/8/128) over an fp8 cache, one
+    fused quantising append + decode. Sampled rows (the shortest, the longest
+    and six more) against the oracle over the dequantised rows, and their new
+    rows' codes and scales bit for bit."""
+    w = W.C3
+    ctx = W.context_lengths(w)
+    nb = W.C3_POOL_BLOCKS
+    bt = W.block_tables(w, ctx, nb)
+    vals = [W.sequence_values(w, b, int(n), 1) for b, n in enumerate(ctx)]
+    say(f"fp8 C3 full size: {w.B} rows, sum ctx {int(ctx.sum())}, {nb} blocks")
+    cache = kvc.PagedKVCache.allocate(nb, w.Hkv, w.D, F8, fill_bits=FILL)
+    btd = torch.from_numpy(bt).cuda()
+    seq = np.concatenate([np.full(int(n) - 1, b, np.int32) for b, n in enumerate(ctx)])
+    pos = np.concatenate([np.arange(int(n) - 1, dtype=np.int32) for n in ctx])
+    s = kvc.slot_mapping(btd, nb, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(),
+                         err_flag=cache.err_flag)
+    kvc.kv_append(cache, s, _dev(np.concatenate([v[0][:-1] for v in vals])),
+                  _dev(np.concatenate([v[1][:-1] for v in vals])))
+    q = _dev(np.stack([v[2][0] for v in vals]))
+    out = kvc.decode_append_attention(cache, q, _dev(np.stack([v[0][-1] for v in vals])),
+                                      _dev(np.stack([v[1][-1] for v in vals])), btd,
+                                      torch.from_numpy(ctx.astype(np.int32)).cuda(),
+                                      int(ctx.max()))
+    torch.cuda.synchronize()
+    assert int(cache.err_flag.item()) == 0
+    got = out.float().cpu().numpy()
+    kc = cache.k_cache.view(torch.uint8).cpu().numpy()
+    ksc = cache.k_scale.cpu().numpy()
+    rng = np.random.default_rng(31)
+    rows = sorted({int(np.argmin(ctx)), int(np.argmax(ctx))}
+                  | set(rng.choice(w.B, 6, False).tolist()))
+    scale = OA.default_scale(w.D)
+    worst = 0.0
+    for b in rows:
+        kb, vb, qb = _bf16(vals[b][0]), _bf16(vals[b][1]), _bf16(vals[b][2][0])
+        kcodes, kscales = OQ.quantize_rows(kb)
+        kq = OQ.dequantize_rows(kcodes, kscales)
+        vq = OQ.dequantize_rows(*OQ.quantize_rows(vb))
+        p = int(ctx[b]) - 1                            # the row the fused launch wrote
+        blk = bt[b, p // 16]
+        assert np.array_equal(kc[blk, :, p % 16, :], kcodes[p]), b
+        assert np.array_equal(ksc[blk, :, p % 16].view(np.uint32), kscales[p].view(np.uint32)), b
+        ref = OA.attend_row(qb.astype(np.float64), kq, vq, scale)
+        worst = max(worst, assert_close(got[b], ref, "bf16", f"fp8 C3 row {b} ctx {ctx[b]}"))
+    say(f"  rows {rows}: max abs err {worst:.2e}")
