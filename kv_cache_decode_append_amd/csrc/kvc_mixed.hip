@@ -37,6 +37,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "kvc_decode_item.h"
 #include "kvc_host.h"
@@ -288,21 +289,24 @@ int mixed_interleave() {
 
 template <typename T, int D, int G>
 int launch_mixed(const MixedArgs& m, int64_t n_items_max, hipStream_t st) {
-  // one resident wave of workgroups: CUs x workgroups per CU (cached per device)
-  static int cached[64][2];
+  // one resident wave of workgroups: CUs x workgroups per CU, cached per device
+  // (as their product; calls from several host threads may race to fill an
+  // entry, with the same value)
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return KVC_ERR_LAUNCH;
-  if (cached[dev][0] == 0) {
+  int resident = cached[dev].load(std::memory_order_relaxed);
+  if (resident == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mixed_step_kernel<T, D, G>,
                                                      kMixThreads, 0) != hipSuccess ||
         cus <= 0 || per_cu <= 0)
       return KVC_ERR_LAUNCH;
-    cached[dev][0] = cus;
-    cached[dev][1] = per_cu;
+    resident = cus * per_cu;
+    cached[dev].store(resident, std::memory_order_relaxed);
   }
-  const int64_t grid = std::min<int64_t>(n_items_max, (int64_t)cached[dev][0] * cached[dev][1]);
+  const int64_t grid = std::min<int64_t>(n_items_max, (int64_t)resident);
   MixedArgs mm = m;
   mm.one_each = grid == n_items_max ? 1 : 0;
   hipLaunchKernelGGL((mixed_step_kernel<T, D, G>), dim3((unsigned)grid), dim3(kMixThreads), 0, st,
