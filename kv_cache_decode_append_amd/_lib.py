@@ -250,6 +250,8 @@ def slot_mapping(block_table: torch.Tensor, num_blocks: int, seq_ids: torch.Tens
     if out is None:
         out = torch.empty(T, dtype=torch.int64, device=block_table.device)
     _need(out, "slot_mapping", torch.int64, 1, block_table.device)
+    if err_flag is not None:
+        _need(err_flag, "err_flag", torch.int32, 1, block_table.device)
     _check("kvc_slot_mapping", LIB.kvc_slot_mapping(
         block_table.data_ptr(), block_table.shape[0], block_table.shape[1], num_blocks,
         seq_ids.data_ptr(), positions.data_ptr(), T, BLOCK_SIZE, out.data_ptr(),
