@@ -228,14 +228,20 @@ def main():
     # the per-launch average is the region's time over the launch count.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    # one more event after every step gives the per-step spread (a timestamp on
+    # the stream between steps; the total is still start to end)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start.record()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         step()
+        marks[i].record()
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    per_step = np.array([t_start.elapsed_time(marks[0])]
+                        + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)])
 
     kv_bytes_layer = int(ctx_np.sum()) * Hkv * D * 2 * 2
     io_bytes_layer = (B * Hq * D * 2 * 2            # q in, out
@@ -255,6 +261,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms_median": round(float(np.median(per_step)), 4),
+        "step_ms_p10": round(float(np.percentile(per_step, 10)), 4),
+        "step_ms_p90": round(float(np.percentile(per_step, 90)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
