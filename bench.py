@@ -243,6 +243,8 @@ def main():
     per_step = np.array([t_start.elapsed_time(marks[0])]
                         + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)])
 
+    ceiling = read_ceiling_gbs(kvc, torch, dev)     # after the timed region
+
     kv_bytes_layer = int(ctx_np.sum()) * Hkv * D * 2 * 2
     io_bytes_layer = (B * Hq * D * 2 * 2            # q in, out
                       + B * Hkv * D * 2 * 2 * 2     # new K/V read and written to the cache
@@ -256,6 +258,8 @@ def main():
         "value": round(kv_gbs, 1),
         "unit": "GB/s",
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
+        "read_ceiling_gbs": round(ceiling, 1),
+        "pct_read_ceiling": round(100.0 * kv_gbs / ceiling, 2),
         "decode_steps_per_s": round(1000.0 / ms_per_step, 2),
         "n_gpus": 1,
         "steps": args.steps,
@@ -287,6 +291,8 @@ def main():
             "traffic": measured_traffic("decode_c3_counters.json"),
             "avg_us": round(dec_avg_us, 2),
             "bytes_per_launch": kv_bytes_layer + io_bytes_layer,
+            "measured_read_ceiling": round(ceiling, 1),
+            "frac_of_measured_ceiling": round(achieved / ceiling, 4),
         },
         "cpu_baseline": None,
     }
@@ -380,6 +386,28 @@ def _timed(fn, steps, warmup):
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / steps
+
+
+def read_ceiling_gbs(kvc, torch, dev, gib=4, reps=10):
+    """HBM read ceiling of this machine: the library's streaming-read probe
+    (128-bit non-temporal loads, front to back) over a `gib` GiB buffer, 16x
+    the 256 MB Infinity Cache, so every byte comes from HBM."""
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = kvc.stream_read(buf)
+    for _ in range(3):
+        kvc.stream_read(buf, out)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        kvc.stream_read(buf, out)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del buf, out
+    torch.cuda.empty_cache()
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 def _base_line(args, metric, value, unit, ms, dtype, config, roofline):

@@ -299,6 +299,18 @@ int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_batch* batc
                              float softmax_scale, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Streaming-read probe, for measurement only: reads `bytes` bytes of device
+ * memory at `data` once, front to back, with 128-bit non-temporal loads (the
+ * plainest read pattern, so its rate over a buffer much larger than the
+ * caches is the HBM read ceiling of the box the kernels above run on).
+ *   data   device memory, 16-byte aligned; bytes a multiple of 16 (0 allowed)
+ *   out    device uint32[kvc_stream_read_groups()]: workgroup g writes the
+ *          wrapping 32-bit sum of the 32-bit words it read, so the sum of all
+ *          entries (mod 2^32) is the sum of all words of the buffer
+ * Async on `stream`; KVC_ERR_NULL / KVC_ERR_SHAPE before any launch. */
+int32_t kvc_stream_read_groups(void);
+int kvc_stream_read(const void* data, size_t bytes, uint32_t* out, void* stream);
+
 /* Static string for a status code. */
 const char* kvc_status_string(int status);
 

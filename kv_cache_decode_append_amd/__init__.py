@@ -34,4 +34,5 @@ from ._lib import (  # noqa: F401
     paged_decode_attention,
     prefill_workspace_bytes,
     slot_mapping,
+    stream_read,
 )

@@ -131,6 +131,8 @@ def _load() -> ctypes.CDLL:
         "kvc_sched_submit": (c_i32, [vp, c_i32, c_i32]),
         "kvc_sched_unfinished": (c_i32, [vp]),
         "kvc_sched_next_step": (c_i32, [vp, ctypes.POINTER(_CStep)]),
+        "kvc_stream_read_groups": (c_i32, []),
+        "kvc_stream_read": (c_int, [vp, c_sz, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -472,6 +474,23 @@ def mixed_step_attention(cache: PagedKVCache, Hq: int, *, q_decode=None, k_new=N
         cache.c, ctypes.byref(b), int(Hq), scale, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream()))
     return out_decode, out_prefill
+
+
+def stream_read(data: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Streaming-read probe (kvc_stream_read): reads every byte of the contiguous
+    GPU tensor `data` once. Returns int32 [kvc_stream_read_groups()] holding each
+    workgroup's wrapping 32-bit sum of the words it read (as int32 bits)."""
+    _need(data, "data")
+    nbytes = data.numel() * data.element_size()
+    groups = int(LIB.kvc_stream_read_groups())
+    if out is None:
+        out = torch.empty(groups, dtype=torch.int32, device=data.device)
+    _need(out, "out", torch.int32, 1, data.device)
+    if out.shape[0] != groups:
+        raise ValueError(f"out must have {groups} entries")
+    _check("kvc_stream_read", LIB.kvc_stream_read(data.data_ptr(), nbytes, out.data_ptr(),
+                                                  _stream()))
+    return out
 
 
 KVC_ERR_NO_BLOCKS = -7
