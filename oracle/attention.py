@@ -21,7 +21,7 @@ G = Hq / Hkv, so that consecutive query heads share one K/V head
 grouped-query attention). Causality (same page, opening section): position t
 sees positions 0..t, itself included, never a later one.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 * the softmax scale is 1/sqrt(D) (scaled dot product), passed explicitly;
 * q-head h uses K/V head h // G (contiguous groups);
 * a decode step appends first, then attends over everything stored, so the

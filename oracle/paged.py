@@ -9,7 +9,7 @@ section "How KV cache memory limits concurrency"); blocks are typically 16
 tokens (daviddominguez page, section "A prefix already in the cache can skip its
 prefill").
 
-Readings (pages silent; listed in the design doc):
+Readings (the pages are silent):
 * pool layout per layer and per K / V: [num_blocks][num_kv_heads][block_size][head_dim];
 * the slot of position p of sequence b is block_table[b][p // bs] * bs + p % bs;
   slot < 0 marks a padding token that writes nothing;

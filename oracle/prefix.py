@@ -19,7 +19,7 @@ and the identifier of the block before it. The plain form of that identity,
 used here, is the whole token prefix a block ends: block i of a prompt is
 known by ``tuple(tokens[:16 * (i + 1)])``.
 
-Readings (the pages are silent; listed in the design doc):
+Readings (the pages are silent):
 
 * at least one token is always left to prefill (its query produces the next
   token), so at most ``(n - 1) // 16`` blocks of an n-token prompt match;

@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 The gouthm page ("The KV cache is not your bottleneck", sections "The setup"
 and "What the profile said") names quantising the KV cache as the way to buy
-memory headroom at a small accuracy cost, and gives no scheme. Readings (listed
-in the design doc), the plainest ones that keep every value of a row recoverable:
+memory headroom at a small accuracy cost, and gives no scheme. Readings, the
+plainest ones that keep every value of a row recoverable:
 
 * format: OCP FP8 E4M3 ("E4M3FN"): 1 sign, 4 exponent (bias 7), 3 mantissa
   bits; normal values m/8 * 2^(e-7) for exponent field e in 1..15 (m in 8..15),

@@ -23,7 +23,7 @@ section "The fix that mattered"):
   step's prefill chunks, taken in admission order, add up to at most the
   budget).
 
-Readings (the pages are silent; listed in the design doc):
+Readings (the pages are silent):
 
 * admission happens at the start of a step, before the step's batch is built;
 * a step's prefill token budget counts prompt tokens only (decode rows are one
