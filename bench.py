@@ -120,16 +120,37 @@ def cpu_baseline(budget_s: float):
         n_steps += 1
     r1 = resource.getrusage(resource.RUSAGE_SELF)
     cpu_s = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
-    # naive recompute-everything loop, a few positions of one sequence
-    k, v, q = W.sequence_values(w, 0, int(ctx[0]), int(ctx[0]))
+    # naive recompute-everything loop at C3: the last 64 rows of one sequence's
+    # full causal attention, timed; row i costs in proportion to its i + 1 keys,
+    # so the whole recompute of a sequence of n tokens costs n(n+1)/2 such units
+    n0 = int(ctx[0])
+    k, v, q = W.sequence_values(w, 0, n0, n0)
     kq = OB.round_bf16(k).astype(np.float64)
     vq = OB.round_bf16(v).astype(np.float64)
     qq = OB.round_bf16(q).astype(np.float64)
-    t0 = time.perf_counter()
     rows = 64
-    OA.causal_rows(qq, kq, vq, int(ctx[0]) - rows, int(ctx[0]) - 1, scale)
-    t_naive_rows = time.perf_counter() - t0
-    naive_step_s = t_naive_rows / rows * int(ctx[0])     # one sequence's full recompute
+    t0 = time.perf_counter()
+    OA.causal_rows(qq, kq, vq, n0 - rows, n0 - 1, scale)
+    per_unit = (time.perf_counter() - t0) / sum(i + 1 for i in range(n0 - rows, n0))
+    naive_seq_s = per_unit * n0 * (n0 + 1) / 2
+    naive_layer_s = per_unit * float(sum(int(c) * (int(c) + 1) / 2 for c in ctx))
+    # the naive and the cached loop over all of the fp32 toy (prompt 16, answer 48)
+    w1 = W.C1
+    n1 = W.C1_PROMPT + W.C1_ANSWER
+    k1, v1, q1 = W.sequence_values(w1, 0, n1, n1)
+    s1 = OA.default_scale(w1.D)
+    t0 = time.perf_counter()
+    OA.generate_uncached(q1, k1, v1, W.C1_PROMPT, W.C1_ANSWER, s1)
+    c1_naive_s = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    OA.generate_cached(q1, k1, v1, W.C1_PROMPT, W.C1_ANSWER, s1)
+    c1_cached_s = time.perf_counter() - t0
+    try:
+        import threadpoolctl
+        blas_threads = max((i.get("num_threads", 0) for i in threadpoolctl.threadpool_info()
+                            if i.get("user_api") == "blas"), default=None)
+    except ImportError:
+        blas_threads = None
     return {
         "value": round(done_bytes / t_run / 1e9, 4),
         "unit": "GB/s",
@@ -139,7 +160,13 @@ def cpu_baseline(budget_s: float):
         "sample": (f"cached-row oracle (fp64 numpy), {n_steps} whole decode steps (64 sequences x "
                    f"{LAYERS} layers), {done_bytes / 1e9:.1f} GB of KV in {t_run:.1f} s"),
         "steps_per_s": round(n_steps / t_run, 4),
-        "naive_oracle_one_sequence_s_extrapolated": round(naive_step_s, 2),
+        "blas_threads": blas_threads,
+        "naive_c3_one_sequence_s_extrapolated": round(naive_seq_s, 2),
+        "naive_c3_layer_64_sequences_s_extrapolated": round(naive_layer_s, 1),
+        "naive_extrapolation": (f"timed: rows {n0 - rows}..{n0 - 1} of sequence 0 (ctx {n0}); "
+                                "scaled by the keys each row of the full recompute sees"),
+        "c1_naive_loop_s": round(c1_naive_s, 4),
+        "c1_cached_loop_s": round(c1_cached_s, 4),
     }
 
 
