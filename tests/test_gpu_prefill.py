@@ -184,3 +184,18 @@ def test_bad_prefix_block_id_is_flagged_not_faulted(kvc, dtype, d, g):
     assert np.isfinite(got).all()
     # sequence 0's table is intact: its rows are still right
     assert_close(got[case.cu[0]:case.cu[1]], case.oracle_rows(0), dtype, "intact sequence 0")
+
+
+@pytest.mark.parametrize("dtype,d,g,prefix,chunk", [("fp32", 128, 1, 40000, 48),
+                                                    ("bf16", 64, 2, 140000, 37),
+                                                    ("bf16", 128, 4, 140000, 21)])
+def test_prefix_past_the_block_row_cache(kvc, dtype, d, g, prefix, chunk):
+    """The workgroup keeps the pool rows of its first blocks in LDS (8,192
+    blocks with buffer->LDS staging, 2,048 with register staging); keys past
+    them look their block up in the table directly. A chunk over a prefix of
+    40,000 (fp32, register staging) or 140,000 (bf16) keys crosses that edge."""
+    say(f"prefill over a {prefix}-key prefix, {dtype} D={d} G={g}, chunk {chunk}")
+    w = W.small_workload(f"pf-long-{dtype}-{d}-{g}", 990 + d + g, B=1, Hq=g, Hkv=1, D=d,
+                         dtype=dtype, sigma=0.5 if dtype == "bf16" else 1.0)
+    case = PrefillCase(w, [prefix], [chunk], W.blocks_for(prefix + chunk) + 16)
+    _check(kvc, case, f"long prefix {dtype} D={d}", pool=False)
