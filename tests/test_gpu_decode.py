@@ -237,3 +237,15 @@ def test_fused_step_equals_separate_calls(kvc, dtype, g, d):
     assert torch.equal(out_a.view(ib), out_b.view(ib))
     assert int(cache_b.err_flag.item()) == 0
     assert_close(out_b.float().cpu().numpy(), case.oracle_out(), dtype, "fused")
+
+
+def test_decode_at_140k_context_many_partitions(kvc):
+    """A 140,000-token sequence beside a 1-token and a 70,001-token one, fused
+    append + decode: the long ones split into many partitions (up to 256
+    blocks each) whose partials the merge pass combines."""
+    say("fused split-K decode at ctx 140,000 / 1 / 70,001, bf16 4/1/128")
+    w = W.small_workload("splitk-140k", 310, B=3, Hq=4, Hkv=1, D=128, dtype="bf16", sigma=0.5)
+    ctx = [140000, 1, 70001]
+    case = DecodeCase(w, ctx, sum(W.blocks_for(c) for c in ctx) + 8)
+    assert kvc.decode_workspace_bytes(3, 4, 128, 140000) > 0
+    _check_case(kvc, case, what="split-K 140k", fused=True)
