@@ -11,13 +11,15 @@ attention (split-K merge pass only when a sequence spans several partitions).
 Inputs are synthetic and resident in HBM before the timed region.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--workload c3-decode|c3-fp8|c4-mixed|c4-mixed-fp8|c5-decode|
-                                c5-prefill|c5-prefill-fp8|prefix-warm|queue-replay]
+                    [--workload c3-decode|c3-fp8|c3-tp8-share|c4-mixed|c4-mixed-fp8|
+                                c5-decode|c5-prefill|c5-prefill-fp8|prefix-warm|queue-replay]
 
 The default workload is the one above (c3-decode). c5-decode (8 sequences at
 32,000 tokens, split-K) and c5-prefill (8 x a 2,048-token chunk over a
 30,000-token cached prefix, MFMA) measure the other kernels of the path on the
 long-context workload; each prints its own line with its own roofline.
+c3-tp8-share runs one GPU's share of the default step when the 8 kv heads are
+spread over 8 GPUs (one kv head and its 4 query heads per layer, same kernel).
 
 Prints ONE JSON line. `value` is KV bytes read per second over the whole step.
 The `roofline` entry is for the per-layer decode launch (paged_decode_kernel,
@@ -48,8 +50,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--workload", default="c3-decode",
-                    choices=["c3-decode", "c3-fp8", "c4-mixed", "c4-mixed-fp8", "c5-decode",
-                             "c5-prefill",
+                    choices=["c3-decode", "c3-fp8", "c3-tp8-share", "c4-mixed", "c4-mixed-fp8",
+                             "c5-decode", "c5-prefill",
                              "c5-prefill-fp8", "prefix-warm", "queue-replay"])
     ap.add_argument("--direct-steps", type=int, default=400,
                     help="queue-replay: leading steps of each continuous plan run for real")
@@ -194,6 +196,8 @@ def main():
         return bench_queue_replay(args)
     if args.workload == "c3-fp8":
         return bench_c3_fp8(args)
+    if args.workload == "c3-tp8-share":
+        return bench_c3_tp8_share(args)
 
     import torch
 
@@ -484,6 +488,66 @@ def bench_c5_decode(args):
                       "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                       "avg_us": round(ms * 1e3, 2), "bytes_per_launch": kv})
+    print(json.dumps(res), flush=True)
+
+
+def bench_c3_tp8_share(args):
+    """One GPU's share of the default step under 8-way kv-head tensor
+    parallelism: the same 64 sequences and context lengths, one kv head and its
+    4 query heads per layer (the other kv heads sit on other GPUs; attention
+    exchanges nothing). Same fused append + decode launch, split over keys as
+    the library decides; 32 layer pools rotated."""
+    import torch
+
+    import kv_cache_decode_append_amd as kvc
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = W.C3
+    B, Hq, Hkv, D = w.B, w.Hq // 8, w.Hkv // 8, w.D
+    L = args.layers
+    ctx_np = W.context_lengths(w)
+    nb = W.C3_POOL_BLOCKS
+    bt = torch.from_numpy(W.block_tables(w, ctx_np, nb)).to(dev)
+    ctx = torch.from_numpy(ctx_np.astype(np.int32)).to(dev)
+    max_ctx = int(ctx_np.max())
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    caches = []
+    for _ in range(L):
+        c = kvc.PagedKVCache.allocate(nb, Hkv, D, torch.bfloat16, device=dev)
+        c.k_cache.normal_(0.0, 0.5, generator=g)
+        c.v_cache.normal_(0.0, 0.5, generator=g)
+        caches.append(c)
+    mk = lambda h: torch.empty(B, h, D, dtype=torch.bfloat16, device=dev).normal_(0, 0.5, generator=g)
+    q, kn, vn = mk(Hq), mk(Hkv), mk(Hkv)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(1, kvc.decode_workspace_bytes(B, Hq, D, max_ctx)), dtype=torch.uint8,
+                     device=dev)
+    ms = _timed(lambda i: kvc.decode_append_attention(caches[i % L], q, kn, vn, bt, ctx, max_ctx,
+                                                      out=out, workspace=ws),
+                args.steps * L, args.warmup * L)
+    errs = [int(c.err_flag.item()) for c in caches]
+    if any(errs) or not torch.isfinite(out.float()).all().item():
+        print(f"bench sanity check failed: err flags {errs}", file=sys.stderr)
+        sys.exit(1)
+    kv = int(ctx_np.sum()) * Hkv * D * 2 * 2
+    # K/V, q, out, the new rows (read and written), block table and lengths
+    per_launch = kv + 2 * B * Hq * D * 2 + 2 * 2 * B * Hkv * D * 2 + bt.numel() * 4 + B * 4
+    step_ms = ms * L
+    gbs = kv * L / (step_ms * 1e-3) / 1e9
+    ach = per_launch / (ms * 1e-3) / 1e9
+    res = _base_line(args, "decode KV-read GB/s, one GPU's share of the B=64 ctx~2k step under "
+                     "kv-head tensor parallelism x8", round(gbs, 1), "GB/s", step_ms, "bf16",
+                     {"workload": "B=64, ctx U[2000,2300], Hq 4 / Hkv 1 (one of 8 kv heads), "
+                                  "head_dim 128, bf16 paged cache, 32 layers",
+                      "B": B, "Hq": Hq, "Hkv": Hkv, "head_dim": D, "layers": L,
+                      "split_workspace_bytes": kvc.decode_workspace_bytes(B, Hq, D, max_ctx)},
+                     {"bound": "hbm", "kernel": "paged_decode_kernel (+ decode_merge_kernel when "
+                      "split)", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                      "avg_us": round(ms * 1e3, 2), "bytes_per_launch": per_launch})
+    res["decode_steps_per_s"] = round(1e3 / step_ms, 2)
     print(json.dumps(res), flush=True)
 
 

@@ -24,7 +24,12 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
   decode_item<T, D, G, kWaves>(a, kvh, b, part, smem);
 }
 
-// One wave per (sequence, query head): combine the partition partials.
+// One wave per (sequence, query head): combine the partition partials with the
+// log-sum-exp rule. Lane j holds partitions j, j + 64, ...: their (m, l) pairs
+// are read in one round and the maximum and the normaliser come from wave
+// reductions. Each lane then adds the partials of its D/64 output dims in
+// partition order, eight partitions' loads in flight at a time, each weight
+// read from the lane that holds its partition.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int32_t hq_all) {
   const int row = blockIdx.x;                 // b * Hq + hq
@@ -33,17 +38,41 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int32_t 
   const int nblk = (ctx + 15) >> 4;
   const int n_used = nblk > 0 ? (nblk + a.part_blocks - 1) / a.part_blocks : 1;
   if (n_used <= 1) return;
+  const int lane = threadIdx.x;
   const float2* ml = a.ws_ml + (size_t)row * a.n_part;
-  float M = -INFINITY;
-  for (int i = 0; i < n_used; ++i) M = fmaxf(M, ml[i].x);
-  float L = 0.f;
-  for (int i = 0; i < n_used; ++i) L += ml[i].y * __builtin_amdgcn_exp2f(ml[i].x - M);
-  const float inv = 1.f / L;
-  for (int d = threadIdx.x; d < D; d += 64) {
-    float A = 0.f;
-    for (int i = 0; i < n_used; ++i)
-      A += __builtin_amdgcn_exp2f(ml[i].x - M) * a.ws_o[((size_t)row * a.n_part + i) * D + d];
-    store_out<ComputeT<T>>(a.out, (size_t)row * D + d, A * inv);
+  const float* po = a.ws_o + (size_t)row * a.n_part * D;
+  float m_lane = -INFINITY;
+  for (int i = lane; i < n_used; i += 64) m_lane = fmaxf(m_lane, ml[i].x);
+  const float M = rows_max(group_max<16>(m_lane));
+  float l_lane = 0.f;
+  for (int i = lane; i < n_used; i += 64) l_lane += ml[i].y * __builtin_amdgcn_exp2f(ml[i].x - M);
+  const float inv = 1.f / rows_sum(group_sum<16>(l_lane));
+  constexpr int E = D >= 64 ? D / 64 : 1;     // output dims per lane
+  const bool has = D >= 64 || lane < D;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int c = 0; c < n_used; c += 64) {      // 64 partitions per round
+    const float w = c + lane < n_used ? __builtin_amdgcn_exp2f(ml[c + lane].x - M) : 0.f;
+    const int n = min(64, n_used - c);
+    for (int j0 = 0; j0 < n; j0 += 8) {
+      float x[8][E];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          x[u][e] = (has && j0 + u < n) ? po[(size_t)(c + j0 + u) * D + lane * E + e] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wu = readlane_f(w, j0 + u);   // 0 past the last partition
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(wu, x[u][e], acc[e]);
+      }
+    }
+  }
+  if (has) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) store_out<ComputeT<T>>(a.out, (size_t)row * D + lane * E + e, acc[e] * inv);
   }
 }
 
