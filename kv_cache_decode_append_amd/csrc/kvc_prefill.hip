@@ -25,27 +25,58 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attention_kernel(PrefillAr
 
 // One wave per (token, query head): combine the key-range partials of a split
 // prefill with the log-sum-exp rule (the same rule the split decode uses).
+// Lane j holds ranges j, j + 64, ...: their (m, l) pairs are read in one round,
+// the maximum and the normaliser come from wave reductions, and each lane adds
+// the partials of its D/64 output dims in range order, eight ranges' loads in
+// flight at a time. A range holding no key of the row (m = -inf) adds nothing.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void prefill_merge_kernel(PrefillArgs a, int32_t hq_all) {
   const size_t row = blockIdx.x;                       // token * Hq + head
   if (row >= (size_t)a.total * hq_all) return;
-  const float2* ml = a.ws_ml + row * a.n_split;
-  float M = -INFINITY;
-  for (int i = 0; i < a.n_split; ++i) M = fmaxf(M, ml[i].x);
-  float L = 0.f;
-  for (int i = 0; i < a.n_split; ++i)
-    if (ml[i].x != -INFINITY) L += ml[i].y * __builtin_amdgcn_exp2f(ml[i].x - M);
-  const float inv = 1.f / L;
-  for (int d = threadIdx.x; d < D; d += 64) {
-    float acc = 0.f;
-    for (int i = 0; i < a.n_split; ++i)
-      if (ml[i].x != -INFINITY)
-        acc += __builtin_amdgcn_exp2f(ml[i].x - M) * a.ws_o[(row * a.n_split + i) * D + d];
-    const float v = acc * inv;
-    if constexpr (ElemBytes<PfComputeT<T>>::value == 4) {
-      reinterpret_cast<float*>(a.out)[row * D + d] = v;
-    } else {
-      reinterpret_cast<uint16_t*>(a.out)[row * D + d] = (uint16_t)f32_to_bf16_bits(v);
+  const int lane = threadIdx.x, n_split = a.n_split;
+  const float2* ml = a.ws_ml + row * n_split;
+  const float* po = a.ws_o + row * n_split * D;
+  float m_lane = -INFINITY;
+  for (int i = lane; i < n_split; i += 64) m_lane = fmaxf(m_lane, ml[i].x);
+  const float M = rows_max(group_max<16>(m_lane));
+  float l_lane = 0.f;
+  for (int i = lane; i < n_split; i += 64)
+    if (ml[i].x != -INFINITY) l_lane += ml[i].y * __builtin_amdgcn_exp2f(ml[i].x - M);
+  const float inv = 1.f / rows_sum(group_sum<16>(l_lane));
+  constexpr int E = D >= 64 ? D / 64 : 1;     // output dims per lane
+  const bool has = D >= 64 || lane < D;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int c = 0; c < n_split; c += 64) {     // 64 ranges per round
+    float w = 0.f;
+    if (c + lane < n_split && ml[c + lane].x != -INFINITY) w = __builtin_amdgcn_exp2f(ml[c + lane].x - M);
+    const int n = min(64, n_split - c);
+    for (int j0 = 0; j0 < n; j0 += 8) {
+      float x[8][E];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          x[u][e] = (has && j0 + u < n) ? po[(size_t)(c + j0 + u) * D + lane * E + e] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j0 + u));
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(wu, wu > 0.f ? x[u][e] : 0.f, acc[e]);
+      }
+    }
+  }
+  if (has) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const size_t o = row * D + lane * E + e;
+      const float v = acc[e] * inv;
+      if constexpr (ElemBytes<PfComputeT<T>>::value == 4) {
+        reinterpret_cast<float*>(a.out)[o] = v;
+      } else {
+        reinterpret_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_bits(v);
+      }
     }
   }
 }
