@@ -37,6 +37,13 @@
  *     table) never touch memory out of bounds: the offending read or write is
  *     skipped (reads yield zero) and, if `err_flag` is non-NULL, a bit is OR-ed
  *     into that device int32 (KVC_DEVERR_*).
+ *   - Alignment: q, k, v, out, k_new, v_new, the K / V pools and workspaces
+ *     must be 16-byte aligned (the kernels move rows in 16-byte chunks, and
+ *     every supported row is a multiple of 16 bytes); int32 arrays (block
+ *     tables, lengths, offsets, ids, positions, err_flag) and the fp8 scale
+ *     pools 4-byte; slot lists (int64) 8-byte. torch allocations and views at
+ *     whole-row offsets satisfy this. A misaligned pointer is rejected with
+ *     KVC_ERR_ALIGN, after every other rule, before any launch.
  *   - Cache layout, per layer and per K / V:
  *         [num_blocks][num_kv_heads][block_size = 16][head_dim]
  *     so one (block, kv-head) tile is contiguous (4 KiB for head_dim 128, bf16).
@@ -80,7 +87,8 @@ enum {
   KVC_ERR_NO_BLOCKS = -7,   /* prefix cache, scheduler: not enough free or reusable blocks */
   KVC_ERR_STATE = -8,       /* prefix cache: a block released or committed that the
                                caller does not hold, or out of range */
-  KVC_ERR_NO_MEMORY = -9    /* host memory ran out (prefix cache, scheduler) */
+  KVC_ERR_NO_MEMORY = -9,   /* host memory ran out (prefix cache, scheduler) */
+  KVC_ERR_ALIGN = -10       /* a pointer is not aligned as the conventions below require */
 };
 
 /* Bits OR-ed into cache->err_flag by kernels that skipped an invalid access. */
@@ -307,7 +315,8 @@ int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_batch* batc
  *   out    device uint32[kvc_stream_read_groups()]: workgroup g writes the
  *          wrapping 32-bit sum of the 32-bit words it read, so the sum of all
  *          entries (mod 2^32) is the sum of all words of the buffer
- * Async on `stream`; KVC_ERR_NULL / KVC_ERR_SHAPE before any launch. */
+ * Async on `stream`; KVC_ERR_NULL / KVC_ERR_SHAPE / KVC_ERR_ALIGN before any
+ * launch. */
 int32_t kvc_stream_read_groups(void);
 int kvc_stream_read(const void* data, size_t bytes, uint32_t* out, void* stream);
 

@@ -200,6 +200,9 @@ extern "C" int kvc_slot_mapping(const int32_t* block_table, int32_t n_seqs, int3
   if (block_size != 16) return KVC_ERR_UNSUPPORTED;
   if (T == 0) return KVC_OK;
   if (!block_table || !seq_ids || !positions || !slot_mapping) return KVC_ERR_NULL;
+  if (!kvc::all_aligned(4, block_table, seq_ids, positions, err_flag) ||
+      !kvc::aligned_to(slot_mapping, 8))
+    return KVC_ERR_ALIGN;
   hipLaunchKernelGGL(kvc::slot_mapping_kernel, dim3((unsigned)kvc::ceil_div(T, 256)), dim3(256), 0,
                      kvc::as_stream(stream), block_table, n_seqs, max_blocks, num_blocks, seq_ids,
                      positions, T, slot_mapping, err_flag);
@@ -213,6 +216,8 @@ extern "C" int kvc_kv_append(const kvc_cache* cache, const int64_t* slot_mapping
   if (T < 0) return KVC_ERR_SHAPE;
   if (T == 0) return KVC_OK;
   if (!slot_mapping || !k || !v) return KVC_ERR_NULL;
+  if (!kvc::cache_aligned(cache) || !kvc::aligned_to(slot_mapping, 8) || !kvc::all_aligned(16, k, v))
+    return KVC_ERR_ALIGN;
   if (cache->dtype == KVC_FP8) {
     const int ncb = cache->head_dim / 8;
     const int64_t n = (int64_t)T * cache->num_kv_heads * ncb;

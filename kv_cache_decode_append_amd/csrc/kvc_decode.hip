@@ -180,6 +180,9 @@ static int decode_entry(const kvc_cache* cache, const void* q, const void* k_new
   const size_t n_rows = (size_t)B * Hq * n_part;
   const size_t need = n_part > 1 ? n_rows * ((size_t)cache->head_dim * 4 + 8) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need)) return KVC_ERR_WORKSPACE;
+  if (!cache_aligned(cache) || !all_aligned(16, q, k_new, v_new, out, workspace) ||
+      !all_aligned(4, block_table, context_lens))
+    return KVC_ERR_ALIGN;
 
   DecodeArgs a;
   a.q = q;

@@ -33,6 +33,21 @@ inline int check_cache(const kvc_cache* c) {
   return KVC_OK;
 }
 
+// Alignment the kernels rely on: 16 bytes for what they move in 16-byte
+// chunks (q, k, v, out, the K / V pools, workspaces), 4 for int32 arrays and
+// the fp8 scale pools, 8 for int64 slot lists. NULL passes (an optional
+// pointer, or one already rejected).
+inline bool aligned_to(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+template <class... P>
+inline bool all_aligned(uintptr_t a, P... p) {
+  return (aligned_to(p, a) && ...);
+}
+inline bool cache_aligned(const kvc_cache* c) {
+  return all_aligned(16, c->k_cache, c->v_cache) && all_aligned(4, c->k_scale, c->v_scale, c->err_flag);
+}
+
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_LAUNCH;
 }

@@ -386,6 +386,13 @@ extern "C" int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_
   }
   const int n_dec = has_dec ? b.n_decode : 0;
   if (!workspace || workspace_bytes < mixed_ws_bytes(n_dec)) return KVC_ERR_WORKSPACE;
+  if (!cache_aligned(cache) || !aligned_to(workspace, 16)) return KVC_ERR_ALIGN;
+  if (has_dec && (!all_aligned(16, b.q_decode, b.k_new, b.v_new, b.out_decode) ||
+                  !all_aligned(4, b.decode_block_table, b.decode_context_lens)))
+    return KVC_ERR_ALIGN;
+  if (has_pf && (!all_aligned(16, b.q_prefill, b.k_prefill, b.v_prefill, b.out_prefill) ||
+                 !all_aligned(4, b.cu_chunk_lens, b.prefix_lens, b.prefill_block_table)))
+    return KVC_ERR_ALIGN;
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
 
   MixedArgs m{};

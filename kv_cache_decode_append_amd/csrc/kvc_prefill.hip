@@ -184,6 +184,9 @@ static int prefill_entry(const kvc_cache* cache, const void* q, const void* k, c
   }
   const size_t need = prefill_ws_bytes(sp, total_tokens, Hq, cache->head_dim);
   if (need > 0 && (!workspace || workspace_bytes < need)) return KVC_ERR_WORKSPACE;
+  if (!cache_aligned(cache) || !all_aligned(16, q, k, v, out, workspace) ||
+      !all_aligned(4, cu_chunk_lens, prefix_lens, block_table))
+    return KVC_ERR_ALIGN;
   hipStream_t s = as_stream(stream);
   st = launch_chunk_append(cache, k, v, n_seqs, cu_chunk_lens, prefix_lens, total_tokens,
                            max_chunk_len, block_table, max_blocks, s);

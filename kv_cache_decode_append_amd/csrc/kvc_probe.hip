@@ -51,7 +51,8 @@ extern "C" int32_t kvc_stream_read_groups(void) { return kvc::kProbeGroups; }
 
 extern "C" int kvc_stream_read(const void* data, size_t bytes, uint32_t* out, void* stream) {
   if (!out || (bytes > 0 && !data)) return KVC_ERR_NULL;
-  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(data) % 16 != 0) return KVC_ERR_SHAPE;
+  if (bytes % 16 != 0) return KVC_ERR_SHAPE;
+  if (!kvc::aligned_to(data, 16) || !kvc::aligned_to(out, 4)) return KVC_ERR_ALIGN;
   hipLaunchKernelGGL(kvc::stream_read_kernel, dim3(kvc::kProbeGroups), dim3(kvc::kProbeThreads), 0,
                      kvc::as_stream(stream), reinterpret_cast<const kvc::u32x4*>(data),
                      (int64_t)(bytes / 16), out);

@@ -23,6 +23,7 @@ extern "C" const char* kvc_status_string(int status) {
     case KVC_ERR_NO_BLOCKS: return "not enough free or reusable blocks";
     case KVC_ERR_STATE: return "block not held, out of range, or cached under another prefix";
     case KVC_ERR_NO_MEMORY: return "host memory ran out";
+    case KVC_ERR_ALIGN: return "pointer not aligned as required (16 bytes for tensors and pools)";
   }
   return "unknown status";
 }

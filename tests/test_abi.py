@@ -127,7 +127,7 @@ def test_zero_sized_calls_launch_nothing():
 
 
 def test_status_strings():
-    for s in range(-9, 1):
+    for s in range(-10, 1):
         assert LIB.kvc_status_string(s)
     assert LIB.kvc_status_string(-99) == b"unknown status"
 
@@ -191,3 +191,53 @@ def test_fp8_cache_rules():
     assert LIB.kvc_mixed_step_attention(ctypes.byref(c32), ctypes.byref(_mixed()), 4, 0.1, 1, 256,
                                         None) == -4
     assert kvc.KVC_FP8 == 2
+
+
+ALIGN = -10
+A = 1 << 12                # an aligned placeholder address (never dereferenced: every call
+                           # below is rejected on the host before any launch)
+
+
+def test_misaligned_pointers_rejected_before_launch():
+    """Each call is valid but for one pointer's alignment (16 bytes for tensors
+    and pools, 4 for int32 arrays, 8 for slot lists), so KVC_ERR_ALIGN is what
+    stops it."""
+    assert kvc._lib.LIB.kvc_status_string(ALIGN) != b"unknown status"
+    c = _cache(k_cache=A, v_cache=A)
+    byref = ctypes.byref(c)
+    # append: k, the slot list, the pool
+    assert LIB.kvc_kv_append(byref, A, A + 2, A, 4, None) == ALIGN
+    assert LIB.kvc_kv_append(byref, A + 4, A, A, 4, None) == ALIGN
+    c_bad = _cache(k_cache=A + 8, v_cache=A)
+    assert LIB.kvc_kv_append(ctypes.byref(c_bad), A, A, A, 4, None) == ALIGN
+    # slot mapping: the int64 output, an int32 input
+    assert LIB.kvc_slot_mapping(A, 1, 4, 8, A, A, 5, 16, A + 4, None, None) == ALIGN
+    assert LIB.kvc_slot_mapping(A, 1, 4, 8, A + 2, A, 5, 16, A, None, None) == ALIGN
+    # decode: q, out, the block table
+    dec = [A, 1, 4, A, 4, A, 64, 0.25, A, None, 0, None]
+    for i, bad in ((0, A + 4), (8, A + 8), (3, A + 2)):
+        args = list(dec)
+        args[i] = bad
+        assert LIB.kvc_paged_decode_attention(byref, *args) == ALIGN, i
+    # fused decode: k_new
+    assert LIB.kvc_decode_append_attention(byref, A, A + 4, A, 1, 4, A, 4, A, 64, 0.25, A, None,
+                                           0, None) == ALIGN
+    # chunked prefill: q, then cu_chunk_lens
+    pf = [A, A, A, 1, A, A, 8, 8, A, 4, 4, 0.25, A, None]
+    for i, bad in ((0, A + 6), (4, A + 1)):
+        args = list(pf)
+        args[i] = bad
+        assert LIB.kvc_chunked_prefill_attention(byref, *args) == ALIGN, i
+    # mixed step: a decode row's query, and the workspace
+    c32 = _cache(k_cache=A, v_cache=A, num_kv_heads=2, head_dim=32)
+    dec_rows = dict(n_decode=2, q_decode=A + 4, k_new=A, v_new=A, decode_block_table=A,
+                    decode_max_blocks=8, decode_context_lens=A, decode_max_context=100,
+                    out_decode=A)
+    ws = kvc.mixed_workspace_bytes(2, 100, 4, 2, 32)
+    f = LIB.kvc_mixed_step_attention
+    assert f(ctypes.byref(c32), ctypes.byref(_mixed(**dec_rows)), 4, 0.1, A, ws, None) == ALIGN
+    assert f(ctypes.byref(c32), ctypes.byref(_mixed(**dict(dec_rows, q_decode=A))), 4, 0.1, A + 8,
+             ws, None) == ALIGN
+    # the read probe: data, then a size that is not a multiple of 16
+    assert LIB.kvc_stream_read(A + 4, 16, A, None) == ALIGN
+    assert LIB.kvc_stream_read(A, 8, A, None) == -2
