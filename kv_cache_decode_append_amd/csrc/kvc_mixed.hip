@@ -243,10 +243,13 @@ __global__ __launch_bounds__(kMixThreads) void mixed_step_kernel(MixedArgs) {
       int my_tid = tid;
       asm volatile("" : "+v"(my_tid));
       if (is_pf) {
-        // later query tiles first: index -> (qt descending, kv head, chunk)
+        // costliest chunks first (at most 64 chunks, else in index order), and
+        // in a chunk later query tiles first: index -> (chunk, qt descending,
+        // kv head)
         const MixedArgs& mi = *fresh_args();
-        const int per = hkv * mi.n_pf;
-        const int qt = mi.pf.n_qt - 1 - idx / per, kvh = (idx % per) % hkv, s = (idx % per) / hkv;
+        const int per = hkv * mi.pf.n_qt;
+        const int rank = idx / per, qt = mi.pf.n_qt - 1 - (idx % per) / hkv, kvh = idx % hkv;
+        const int s = mi.n_pf <= kMaxRankedSeqs ? seq_with_cost_rank(mi.pf, mi.n_pf, rank) : rank;
         prefill_item<T, D, G>(mi.pf, qt + mi.pf.n_qt * (kvh + hkv * s), smem, my_tid);
       } else {
         const MixedArgs& mi = *fresh_args();

@@ -11,15 +11,16 @@
 
 namespace kvc {
 
-constexpr int kMaxRankedSeqs = 64;    // one per lane of a wave
+constexpr int kCUs = 256;   // MI355X compute units, one prefill workgroup each
 
 // Work item of this workgroup. Workgroups are dealt round-robin to the 8 XCDs,
 // and each XCD runs the items it is given in order. A group (the query tiles
 // of one sequence and kv head) stays on one XCD, so its tiles share that L2
 // while they sweep the same keys. Handing each XCD a contiguous run of groups
 // would, for a few sequences of different lengths, leave the XCDs that drew
-// the long ones working alone at the end; so (when the groups fill the XCDs
-// evenly and there are at most 64 sequences) the groups are ranked by cost,
+// the long ones working alone at the end; so (when there are more items than
+// CUs, the groups fill the XCDs evenly and there are at most 64 sequences) the
+// groups are ranked by cost,
 // chunk length x mean keys per query, and dealt to the XCDs in snake order,
 // costliest first: every XCD gets an even share and starts with its largest.
 __device__ __forceinline__ int prefill_work(const PrefillArgs& a) {
@@ -28,26 +29,13 @@ __device__ __forceinline__ int prefill_work(const PrefillArgs& a) {
   const int ipg = a.n_qt * a.n_split;                 // items per group: qt fastest, then split
   const int n_groups = a.n_work / ipg;
   const int n_seqs = n_groups / a.hkv;
-  if (n_groups % 8 != 0 || n_seqs > kMaxRankedSeqs || per_xcd * 8 != a.n_work)
+  // with no more items than CUs every workgroup has a CU of its own and the
+  // order does not matter; the ranking would only add a read before the start
+  if (a.n_work <= kCUs || n_groups % 8 != 0 || n_seqs > kMaxRankedSeqs || per_xcd * 8 != a.n_work)
     return x * per_xcd + j;
   const int k = j / ipg, t = j % ipg;
   const int r = 8 * k + ((k & 1) ? 7 - x : x);       // rank of the group, 0 = costliest
-  const int seq_rank = r / a.hkv, kvh = r % a.hkv;
-  // lane i ranks sequence i: the sequences costlier than it, ties by index
-  const int lane = threadIdx.x & 63;
-  int64_t cost = -1;
-  if (lane < n_seqs) {
-    const int64_t c = a.cu[lane + 1] - a.cu[lane];
-    cost = c * (2 * (int64_t)a.prefix[lane] + c);
-  }
-  const int lo = (int)(uint32_t)cost, hi = (int)(cost >> 32);
-  int rank = 0;
-  for (int m = 0; m < n_seqs; ++m) {
-    const int64_t cm = (int64_t)(((uint64_t)(uint32_t)__shfl(hi, m, 64) << 32) | (uint32_t)__shfl(lo, m, 64));
-    rank += (cm > cost || (cm == cost && m < lane)) ? 1 : 0;
-  }
-  const uint64_t hit = __ballot(lane < n_seqs && rank == seq_rank);   // exactly one lane
-  const int s = __builtin_ctzll(hit);
+  const int s = seq_with_cost_rank(a, n_seqs, r / a.hkv), kvh = r % a.hkv;
   return t + ipg * (kvh + a.hkv * s);
 }
 

@@ -155,6 +155,28 @@ struct PrefillArgs {
   const float* vs;
 };
 
+constexpr int kMaxRankedSeqs = 64;    // one per lane of a wave
+
+// The sequence whose prefill cost (chunk length x mean keys per query) has rank
+// `rank` among the first n_seqs <= 64 (0 = costliest, ties by index). Every
+// wave computes it alone: lane i counts the sequences costlier than i.
+__device__ __forceinline__ int seq_with_cost_rank(const PrefillArgs& a, int n_seqs, int rank) {
+  const int lane = threadIdx.x & 63;
+  int64_t cost = -1;
+  if (lane < n_seqs) {
+    const int64_t c = a.cu[lane + 1] - a.cu[lane];
+    cost = c * (2 * (int64_t)a.prefix[lane] + c);
+  }
+  const int lo = (int)(uint32_t)cost, hi = (int)(cost >> 32);
+  int mine = 0;
+  for (int m = 0; m < n_seqs; ++m) {
+    const int64_t cm = (int64_t)(((uint64_t)(uint32_t)__shfl(hi, m, 64) << 32) | (uint32_t)__shfl(lo, m, 64));
+    mine += (cm > cost || (cm == cost && m < lane)) ? 1 : 0;
+  }
+  const uint64_t hit = __ballot(lane < n_seqs && mine == rank);   // exactly one lane
+  return __builtin_ctzll(hit);
+}
+
 template <typename T>
 __device__ __forceinline__ void store4(void* out, size_t idx, const f32x4& v, float inv);
 template <>
