@@ -249,3 +249,43 @@ def test_decode_at_140k_context_many_partitions(kvc):
     case = DecodeCase(w, ctx, sum(W.blocks_for(c) for c in ctx) + 8)
     assert kvc.decode_workspace_bytes(3, 4, 128, 140000) > 0
     _check_case(kvc, case, what="split-K 140k", fused=True)
+
+
+def test_split_k_agrees_with_one_partition(kvc):
+    """The same 3,000-token sequence decoded as row 0 of a 64-row batch (one
+    partition: the batch already fills 512 workgroups) and alone (12
+    partitions and the merge): each within the oracle's tolerance, and within
+    it of each other."""
+    say("split-K vs one partition, fp32 32/8/128, ctx 3,000")
+    w = W.small_workload("split-vs-one", 320, B=64, Hq=32, Hkv=8, D=128, dtype="fp32")
+    ctx = [3000] + [300] * 63
+    batch = DecodeCase(w, ctx, sum(W.blocks_for(c) for c in ctx) + 8)
+    alone = DecodeCase(w, [3000], W.blocks_for(3000) + 8)     # row 0's values, same seed
+    assert np.array_equal(alone.q[0], batch.q[0])
+    _, ob = batch.run_gpu(kvc)
+    _, oa = alone.run_gpu(kvc)
+    ref = alone.oracle_out()
+    got_b, got_a = ob.float().cpu().numpy()[:1], oa.float().cpu().numpy()
+    assert_close(got_b, ref, "fp32", "one partition")
+    assert_close(got_a, ref, "fp32", "12 partitions")
+    assert_close(got_a, got_b, "fp32", "split vs one partition")
+
+
+def test_gqa_equals_mha_over_repeated_heads(kvc):
+    """Grouped-query attention is multi-head attention with each K/V head
+    repeated G times: the G = 4 decode over 2 kv heads and the G = 1 decode over
+    the 8 heads made by repeating them agree (fp32)."""
+    say("GQA 8/2 vs MHA 8/8 over repeated K/V heads, fp32 D=64")
+    wg = W.small_workload("gqa-vs-mha", 330, B=4, Hq=8, Hkv=2, D=64, dtype="fp32")
+    wm = W.small_workload("gqa-vs-mha-rep", 331, B=4, Hq=8, Hkv=8, D=64, dtype="fp32")
+    ctx = [1, 17, 300, 1000]
+    g = DecodeCase(wg, ctx, 200)
+    m = DecodeCase(wm, ctx, 200)
+    m.q = g.q.copy()
+    m.k = [np.repeat(k, 4, axis=1) for k in g.k]
+    m.v = [np.repeat(v, 4, axis=1) for v in g.v]
+    _, og = g.run_gpu(kvc)
+    _, om = m.run_gpu(kvc)
+    got_g, got_m = og.float().cpu().numpy(), om.float().cpu().numpy()
+    assert_close(got_g, g.oracle_out(), "fp32", "GQA")
+    assert_close(got_m, got_g, "fp32", "MHA over repeated heads vs GQA")
