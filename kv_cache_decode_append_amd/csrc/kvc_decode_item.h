@@ -342,6 +342,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     }
   };
   float cur_sk = 0.f, cur_sv = 0.f;   // fp8: the block's row scales, lane l: token l % 16
+  u32x2 cur_v8[S::NI];                 // fp8: the block's V codes (the same units as vb)
   // One block. TAIL marks the sequence's last block, the only one that can be
   // partial or hold the appended token; every other block skips the masking
   // and substitution code entirely.
@@ -356,7 +357,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
           kb[j] = k_new_c;
           vb[j] = v_new_c;
         }
-        if (lb * 16 + tk >= ctx) vb[j] = u32x4{0u, 0u, 0u, 0u};   // unwritten rows may hold NaN
+        if (lb * 16 + tk >= ctx) {                                 // unwritten rows may hold NaN
+          if constexpr (F8) cur_v8[j] = u32x2{0u, 0u};
+          else vb[j] = u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
     // K tile -> LDS, chunk c of token t at chunk slot c ^ (t % NC)
@@ -460,20 +464,36 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
 #pragma unroll
       for (int m = 0; m < S::NI / 2; ++m) {
         const int pr = m * S::TPI + lane / S::NC;
-        const u32x4 va = vb[2 * m], vbb = vb[2 * m + 1];
         uint32_t pp[G];
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) pp[hh] = p32[pr * G + hh];
+        // x[e] = (token a, token b) of dim e as a bf16 pair
+        uint32_t x[8];
+        if constexpr (F8) {
+          // interleave the two tokens' code bytes, then convert pairs: each
+          // E4M3 code is a bf16 value, so the pairs equal the bf16 path's
+          const u32x2 ca = cur_v8[2 * m], cb = cur_v8[2 * m + 1];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t xlo = __builtin_amdgcn_perm(vbb[k], va[k], 0x05040100u);
-          const uint32_t xhi = __builtin_amdgcn_perm(vbb[k], va[k], 0x07060302u);
+          for (int w = 0; w < 2; ++w) {
+            const uint32_t lo = __builtin_amdgcn_perm(cb[w], ca[w], 0x05010400u);   // a0 b0 a1 b1
+            const uint32_t hi = __builtin_amdgcn_perm(cb[w], ca[w], 0x07030602u);   // a2 b2 a3 b3
+            x[4 * w + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false));
+            x[4 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true));
+            x[4 * w + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false));
+            x[4 * w + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true));
+          }
+        } else {
+          const u32x4 va = vb[2 * m], vbb = vb[2 * m + 1];
 #pragma unroll
-          for (int hh = 0; hh < G; ++hh) {
-            acc[hh][2 * k] = dot2_bf16(pp[hh], xlo, acc[hh][2 * k]);
-            acc[hh][2 * k + 1] = dot2_bf16(pp[hh], xhi, acc[hh][2 * k + 1]);
+          for (int k = 0; k < 4; ++k) {
+            x[2 * k] = __builtin_amdgcn_perm(vbb[k], va[k], 0x05040100u);
+            x[2 * k + 1] = __builtin_amdgcn_perm(vbb[k], va[k], 0x07060302u);
           }
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) acc[hh][e] = dot2_bf16(pp[hh], x[e], acc[hh][e]);
       }
     } else {
 #pragma unroll
@@ -492,13 +512,14 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     }
   };
 
-  // fp8: convert a ring slot's codes to the bf16 tile the shared path reads
-  // (with the new token's codes and scales in place for the tail block), then
-  // process it.
+  // fp8: convert a ring slot's K codes to the bf16 tile the shared path reads
+  // and hand its V codes to the PV product as they are (with the new token's
+  // codes and scales in place for the tail block), then process it.
   auto process8 = [&](auto tail_tag, u32x2 (&kr)[S::NI], u32x2 (&vr)[S::NI], float sk, float sv,
                       int i) {
     constexpr bool TAIL = decltype(tail_tag)::value;
-    u32x4 kb[S::NI], vb[S::NI];
+    static_assert(S::DOT2_PV, "fp8 V codes go straight into the packed PV product");
+    u32x4 kb[S::NI], vb[S::NI] = {};   // vb unused: PV reads the codes in cur_v8
 #pragma unroll
     for (int j = 0; j < S::NI; ++j) {
       u32x2 kx = kr[j], vx = vr[j];
@@ -509,7 +530,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
         }
       }
       kb[j] = e4m3x8_to_bf16x8(kx);
-      vb[j] = e4m3x8_to_bf16x8(vx);
+      cur_v8[j] = vx;
     }
     cur_sk = sk;
     cur_sv = sv;
