@@ -125,18 +125,12 @@ int dispatch_decode(const DecodeArgs& a, int dtype, int D, int B, int G, hipStre
 // Blocks per partition. Every partition costs a pipeline fill, an LDS merge
 // and (when a sequence has several) a partial write plus the merge pass, so a
 // sequence is split only as far as needed to give the chip about two resident
-// workgroups per CU (512 on MI355X's 256 CUs). B=64 x 8 kv heads already fills
+// workgroups per CU (512 on a 256-CU MI355X). B=64 x 8 kv heads already fills
 // that unsplit; 8 sequences at 32k tokens are split 8 ways.
-constexpr int kTargetWorkgroups = 512;
-
-int decode_part_blocks(int B, int hkv, int nblk_max) {
-  static const int forced = [] {
-    const char* e = getenv("KVC_DECODE_PART_BLOCKS");
-    return e ? atoi(e) : 0;
-  }();
-  if (forced >= kMinPartBlocks) return forced < kMaxPartBlocks ? forced : kMaxPartBlocks;
+int decode_part_blocks(int B, int hkv, int nblk_max, int cus) {
+  const int64_t target = 2 * (int64_t)cus;
   const int64_t units = (int64_t)B * hkv;
-  int64_t n_part = (kTargetWorkgroups + units - 1) / units;
+  int64_t n_part = (target + units - 1) / units;
   const int64_t max_parts = (nblk_max + kMinPartBlocks - 1) / kMinPartBlocks;
   if (n_part > max_parts) n_part = max_parts;
   if (n_part < 1) n_part = 1;
@@ -174,15 +168,22 @@ static int decode_entry(const kvc_cache* cache, const void* q, const void* k_new
   if (B == 0) return KVC_OK;
   if (!q || !block_table || !context_lens || !out) return KVC_ERR_NULL;
 
-  const int nblk_max = (int)ceil_div(max_context_len, 16);
-  const int pb = decode_part_blocks(B, cache->num_kv_heads, nblk_max);
-  const int n_part = nblk_max > 0 ? (int)ceil_div(nblk_max, pb) : 1;
-  const size_t n_rows = (size_t)B * Hq * n_part;
-  const size_t need = n_part > 1 ? n_rows * ((size_t)cache->head_dim * 4 + 8) : 0;
-  if (need > 0 && (!workspace || workspace_bytes < need)) return KVC_ERR_WORKSPACE;
+  // the workspace rule is the size query's (it covers the most partitions
+  // any device would use), so validation does not depend on the device
+  const size_t ws_rule = kvc_decode_workspace_bytes(B, Hq, cache->head_dim, max_context_len);
+  if (ws_rule > 0 && (!workspace || workspace_bytes < ws_rule)) return KVC_ERR_WORKSPACE;
   if (!cache_aligned(cache) || !all_aligned(16, q, k_new, v_new, out, workspace) ||
       !all_aligned(4, block_table, context_lens))
     return KVC_ERR_ALIGN;
+
+  const int nblk_max = (int)ceil_div(max_context_len, 16);
+  const DeviceInfo dev = device_info();
+  if (dev.cus == 0) return KVC_ERR_LAUNCH;
+  const int pb = decode_part_blocks(B, cache->num_kv_heads, nblk_max, dev.cus);
+  const int n_part = nblk_max > 0 ? (int)ceil_div(nblk_max, pb) : 1;
+  const size_t n_rows = (size_t)B * Hq * n_part;
+  const size_t need = n_part > 1 ? n_rows * ((size_t)cache->head_dim * 4 + 8) : 0;
+  if (need > ws_rule) return KVC_ERR_WORKSPACE;   // cannot happen: pb >= kMinPartBlocks
 
   DecodeArgs a;
   a.q = q;

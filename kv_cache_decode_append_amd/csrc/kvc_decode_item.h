@@ -108,13 +108,19 @@ struct DecodeArgs {
 };
 
 // Context length the kernels use: clamped to what the grid and table cover.
-__device__ __forceinline__ int effective_ctx(const DecodeArgs& a, int b, bool report) {
+// `in_bounds` (optional) says whether the caller's length needed no clamping; a
+// clamped row is attended over the clamped length but gets no append, since
+// its new token's position lies past what the table or the bound covers.
+__device__ __forceinline__ int effective_ctx(const DecodeArgs& a, int b, bool report,
+                                             bool* in_bounds = nullptr) {
   int ctx = a.ctx_lens[b];
   const int cap = min(a.max_ctx, a.max_blocks * 16);
-  if (ctx > cap || ctx < 0) {
+  const bool ok = ctx >= 0 && ctx <= cap;
+  if (!ok) {
     if (report) flag_error(a.err, KVC_DEVERR_CONTEXT);
     ctx = ctx < 0 ? 0 : cap;
   }
+  if (in_bounds) *in_bounds = ok;
   return ctx;
 }
 
@@ -190,7 +196,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hq_all = a.hkv * G;
 
-  const int ctx = effective_ctx(a, b, part == 0 && kvh == 0 && tid == 0);
+  bool ctx_ok;
+  const int ctx = effective_ctx(a, b, part == 0 && kvh == 0 && tid == 0, &ctx_ok);
   const int nblk = (ctx + 15) >> 4;
   const int n_used = nblk > 0 ? (nblk + a.part_blocks - 1) / a.part_blocks : 1;
   if (part >= n_used) return;
@@ -309,8 +316,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
   // here, before the pipelined loop (memory operations inside the loop would
   // make the compiler wait on the whole prefetch ring), substituted in
   // registers when the last block is processed, and stored to the cache after
-  // the loop. Only the workgroup whose partition holds the last block does so.
-  const bool fuse = FUSE && a.k_new != nullptr && part == n_used - 1;
+  // the loop. Only the workgroup whose partition holds the last block does so,
+  // and nothing is appended for a row whose length had to be clamped (the
+  // clamped position holds a valid cached token).
+  const bool fuse = FUSE && ctx_ok && a.k_new != nullptr && part == n_used - 1;
   const int t_new = (ctx - 1) & 15;
   u32x4 k_new_c = u32x4{0u, 0u, 0u, 0u}, v_new_c = u32x4{0u, 0u, 0u, 0u};
   auto load_new = [&] {

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kvc.h"
 
 namespace kvc {
@@ -55,5 +57,30 @@ inline int launch_status() {
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute units and XCDs (accelerator complex dies, each with its own L2) of
+// the current device, queried once per device and cached; {0, 0} if the
+// runtime cannot say. Calls from several host threads may race to fill an
+// entry, with the same values.
+struct DeviceInfo {
+  int cus;
+  int xcds;
+};
+inline DeviceInfo device_info() {
+  static std::atomic<int> cached_cus[64], cached_xcds[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return {0, 0};
+  int cus = cached_cus[dev].load(std::memory_order_relaxed);
+  int xcds = cached_xcds[dev].load(std::memory_order_relaxed);
+  if (cus == 0 || xcds == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess ||
+        cus <= 0 || xcds <= 0)
+      return {0, 0};
+    cached_cus[dev].store(cus, std::memory_order_relaxed);
+    cached_xcds[dev].store(xcds, std::memory_order_relaxed);
+  }
+  return {cus, xcds};
+}
 
 }  // namespace kvc

@@ -34,8 +34,6 @@
 // before any that wait, and the wait is bounded anyway. The queue header is
 // reset by the last workgroup to leave.
 
-#include <stdlib.h>
-
 #include <algorithm>
 #include <atomic>
 
@@ -75,7 +73,6 @@ struct MixedArgs {
   int32_t n_phase0;     // plan + n_pf * n_slices
   int32_t n_pf_items;   // n_qt * hkv * n_pf
   int32_t n_dec_items;  // hkv * n_dec
-  int32_t interleave;   // 1: prefill and decode items interleaved, 0: prefill first
   int32_t one_each;     // the grid has a workgroup per item: no queue
 };
 
@@ -113,13 +110,16 @@ __device__ __forceinline__ void plan_decode(const MixedArgs& m, int32_t* scratch
 // The new K/V of decode row b for kv head kvh at position context_len - 1,
 // written by the decode item itself before it reads the row (a workgroup
 // barrier orders the two); an fp8 cache gets the row's codes and scale, made
-// by the first D / 8 lanes together. A row with an empty context holds no token.
+// by the first D / 8 lanes together. A row with an empty context holds no token,
+// and a row whose length exceeds the bounds gets no append (the decode item
+// flags it).
 template <typename T, int D>
 __device__ __forceinline__ void append_decode_row(const MixedArgs& m, int b, int kvh, int tid) {
   const DecodeArgs& a = m.dec;
   if (tid < m.nc) {
-    const int ctx = effective_ctx(a, b, false);
-    if (ctx >= 1) {
+    bool ok;
+    const int ctx = effective_ctx(a, b, false, &ok);
+    if (ok && ctx >= 1) {
       const int32_t* bt_row = a.bt + (size_t)b * a.max_blocks;
       int bad;
       if constexpr (std::is_same_v<T, fp8_tag>)
@@ -208,16 +208,10 @@ __global__ __launch_bounds__(kMixThreads) void mixed_step_kernel(MixedArgs) {
       const int k = item - m.n_phase0;
       const int64_t n_pf = m.n_pf_items, n_all = n_pf + m.n_dec_items;
       if (k >= n_all) break;
-      bool is_pf;
-      int idx;
-      if (m.interleave) {
-        const int pf_before = (int)((int64_t)k * n_pf / n_all);
-        is_pf = (int)((int64_t)(k + 1) * n_pf / n_all) > pf_before;
-        idx = is_pf ? pf_before : k - pf_before;
-      } else {
-        is_pf = k < n_pf;
-        idx = is_pf ? k : k - (int)n_pf;
-      }
+      // prefill items first: the largest items (late query tiles over long
+      // prefixes) start earliest and the short decode items fill the tail
+      const bool is_pf = k < n_pf;
+      const int idx = is_pf ? k : k - (int)n_pf;
       if (!open && (is_pf || m.plan)) {
         if (tid == 0) {
           int spins = 0;
@@ -276,19 +270,6 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace: the 256-byte queue header, then the decode row order.
 size_t mixed_ws_bytes(int n_dec) { return 256 + align256((size_t)n_dec * 4); }
-
-// Prefill items first, then decode items (default), or the two interleaved in
-// proportion to their counts (KVC_MIXED_ORDER=1). On the skewed 210-sequence
-// step prefill first is faster (2.65 against 2.76 ms per layer): the largest
-// items (late query tiles over long prefixes) start earliest and the short
-// decode items fill the tail.
-int mixed_interleave() {
-  static const int v = [] {
-    const char* e = getenv("KVC_MIXED_ORDER");
-    return e && atoi(e) == 1 ? 1 : 0;
-  }();
-  return v;
-}
 
 template <typename T, int D, int G>
 int launch_mixed(const MixedArgs& m, int64_t n_items_max, hipStream_t st) {
@@ -467,6 +448,5 @@ extern "C" int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_
   m.n_phase0 = (int)n_phase0;
   m.n_pf_items = p.n_work;
   m.n_dec_items = n_dec * hkv;
-  m.interleave = mixed_interleave();
   return dispatch_mixed(m, cache->dtype, D, G, n_items_max, as_stream(stream));
 }

@@ -11,30 +11,29 @@
 
 namespace kvc {
 
-constexpr int kCUs = 256;   // MI355X compute units, one prefill workgroup each
-
-// Work item of this workgroup. Workgroups are dealt round-robin to the 8 XCDs,
-// and each XCD runs the items it is given in order. A group (the query tiles
-// of one sequence and kv head) stays on one XCD, so its tiles share that L2
-// while they sweep the same keys. Handing each XCD a contiguous run of groups
-// would, for a few sequences of different lengths, leave the XCDs that drew
-// the long ones working alone at the end; so (when there are more items than
-// CUs, the groups fill the XCDs evenly and there are at most 64 sequences) the
-// groups are ranked by cost,
-// chunk length x mean keys per query, and dealt to the XCDs in snake order,
-// costliest first: every XCD gets an even share and starts with its largest.
+// Work item of this workgroup. Workgroups are dealt round-robin to the XCDs
+// (8 on MI355X), and each XCD runs the items it is given in order. A group
+// (the query tiles of one sequence and kv head) stays on one XCD, so its tiles
+// share that L2 while they sweep the same keys. Handing each XCD a contiguous
+// run of groups would, for a few sequences of different lengths, leave the
+// XCDs that drew the long ones working alone at the end; so (when there are
+// more items than CUs, the groups fill the XCDs evenly and there are at most
+// 64 sequences) the groups are ranked by cost, chunk length x mean keys per
+// query, and dealt to the XCDs in snake order, costliest first: every XCD gets
+// an even share and starts with its largest.
 __device__ __forceinline__ int prefill_work(const PrefillArgs& a) {
-  const int x = blockIdx.x % 8, j = blockIdx.x / 8;
-  const int per_xcd = gridDim.x / 8;
+  const int nx = a.n_xcd;
+  const int x = blockIdx.x % nx, j = blockIdx.x / nx;
+  const int per_xcd = gridDim.x / nx;
   const int ipg = a.n_qt * a.n_split;                 // items per group: qt fastest, then split
   const int n_groups = a.n_work / ipg;
   const int n_seqs = n_groups / a.hkv;
   // with no more items than CUs every workgroup has a CU of its own and the
   // order does not matter; the ranking would only add a read before the start
-  if (a.n_work <= kCUs || n_groups % 8 != 0 || n_seqs > kMaxRankedSeqs || per_xcd * 8 != a.n_work)
+  if (a.n_work <= a.n_cus || n_groups % nx != 0 || n_seqs > kMaxRankedSeqs || per_xcd * nx != a.n_work)
     return x * per_xcd + j;
   const int k = j / ipg, t = j % ipg;
-  const int r = 8 * k + ((k & 1) ? 7 - x : x);       // rank of the group, 0 = costliest
+  const int r = nx * k + ((k & 1) ? nx - 1 - x : x);  // rank of the group, 0 = costliest
   const int s = seq_with_cost_rank(a, n_seqs, r / a.hkv), kvh = r % a.hkv;
   return t + ipg * (kvh + a.hkv * s);
 }
@@ -110,7 +109,7 @@ int launch_prefill(PrefillArgs a, int n_seqs, int max_chunk, hipStream_t st) {
   using S = PfShape<PfComputeT<T>, D, G>;
   a.n_qt = (max_chunk + S::MP - 1) / S::MP;
   a.n_work = a.n_qt * a.n_split * a.hkv * n_seqs;
-  const int grid = (a.n_work + 7) / 8 * 8;           // whole XCD rounds
+  const int grid = (a.n_work + a.n_xcd - 1) / a.n_xcd * a.n_xcd;   // whole XCD rounds
   hipLaunchKernelGGL((prefill_attention_kernel<T, D, G>), dim3(grid), dim3(kPfThreads), 0, st, a);
   if (hipGetLastError() != hipSuccess) return KVC_ERR_LAUNCH;
   if (a.n_split > 1) {
@@ -211,6 +210,8 @@ static int prefill_entry(const kvc_cache* cache, const void* q, const void* k, c
   if (!cache_aligned(cache) || !all_aligned(16, q, k, v, out, workspace) ||
       !all_aligned(4, cu_chunk_lens, prefix_lens, block_table))
     return KVC_ERR_ALIGN;
+  const DeviceInfo dev = device_info();
+  if (dev.cus == 0) return KVC_ERR_LAUNCH;
   hipStream_t s = as_stream(stream);
   st = launch_chunk_append(cache, k, v, n_seqs, cu_chunk_lens, prefix_lens, total_tokens,
                            max_chunk_len, block_table, max_blocks, s);
@@ -231,6 +232,8 @@ static int prefill_entry(const kvc_cache* cache, const void* q, const void* k, c
   a.max_chunk = max_chunk_len;
   a.n_split = sp.n_split;
   a.split_tiles = sp.split_tiles;
+  a.n_cus = dev.cus;
+  a.n_xcd = dev.xcds;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.ks = cache->k_scale;
   a.vs = cache->v_scale;

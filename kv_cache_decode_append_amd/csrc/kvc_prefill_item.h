@@ -148,6 +148,8 @@ struct PrefillArgs {
   int32_t n_split;    // key-range splits per query tile (1: no split, rows written directly)
   int32_t split_tiles;  // key tiles per split
   int32_t n_work;     // n_qt * n_split * hkv * n_seqs
+  int32_t n_cus;      // compute units and XCDs of the device (the workgroup deal)
+  int32_t n_xcd;
   float scale_log2;
   float* ws_o;        // split partials: [total][Hq][n_split][D] fp32, unnormalised
   float2* ws_ml;      // [total][Hq][n_split] (running max in log2 units, row sum)
