@@ -28,7 +28,9 @@
  * Conventions shared by every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller. The library
  *     never allocates, frees or synchronises; it keeps no state between calls
- *     and is safe to call from several host threads.
+ *     (beyond cached device properties and the built-in scratch array of
+ *     kvc_decode_append_attention_noalloc) and is safe to call from several
+ *     host threads.
  *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
  *     enqueues work on it and returns.
  *   - Host-side validation happens before any launch: on a negative status
@@ -88,8 +90,13 @@ enum {
   KVC_ERR_STATE = -8,       /* prefix cache: a block released or committed that the
                                caller does not hold, or out of range */
   KVC_ERR_NO_MEMORY = -9,   /* host memory ran out (prefix cache, scheduler) */
-  KVC_ERR_ALIGN = -10       /* a pointer is not aligned as the conventions below require */
+  KVC_ERR_ALIGN = -10,      /* a pointer is not aligned as the conventions below require */
+  KVC_ERR_SCRATCH = -11     /* kvc_decode_append_attention_noalloc: the call needs more than
+                               the library's built-in KVC_SCRATCH_BYTES of scratch */
 };
+
+/* Size of the per-device scratch array of kvc_decode_append_attention_noalloc. */
+#define KVC_SCRATCH_BYTES ((size_t)16 << 20)
 
 /* Bits OR-ed into cache->err_flag by kernels that skipped an invalid access. */
 enum {
@@ -189,6 +196,28 @@ int kvc_decode_append_attention(const kvc_cache* cache, const void* q, const voi
                                 const int32_t* context_lens, int32_t max_context_len,
                                 float softmax_scale, void* out, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* kvc_decode_append_attention for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc) and so cannot provide a workspace: the split-K partial results go
+ * to a scratch array inside the library instead, KVC_SCRATCH_BYTES (16 MiB) per
+ * device, held from the first call on a device until the process ends. The
+ * call allocates nothing; the caller still passes every input and output.
+ * Arguments, outputs and results as kvc_decode_append_attention (same kernels,
+ * same bits), without the workspace.
+ *   Returns KVC_ERR_SCRATCH, before any launch, when the split-K partials
+ *   would exceed KVC_SCRATCH_BYTES (B * Hq * partitions * (4 * head_dim + 8)
+ *   bytes, partitions chosen as for kvc_decode_append_attention; C5's 8 x
+ *   32,000-token decode needs about 1 MiB).
+ * Every call on a device shares that device's array (no initialisation is
+ * needed: each call writes the partials it reads), so calls that overlap on
+ * one device, on different streams or from different host threads, race and
+ * must be ordered by the caller. */
+int kvc_decode_append_attention_noalloc(const kvc_cache* cache, const void* q, const void* k_new,
+                                        const void* v_new, int32_t B, int32_t Hq,
+                                        const int32_t* block_table, int32_t max_blocks,
+                                        const int32_t* context_lens, int32_t max_context_len,
+                                        float softmax_scale, void* out, void* stream);
 
 /* Chunked prefill: write a prompt chunk's K/V into the cache, then causal
  * attention of each chunk position over the cached prefix plus the chunk's

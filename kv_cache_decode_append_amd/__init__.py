@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     Scheduler,
     chunked_prefill_attention,
     decode_append_attention,
+    decode_append_attention_noalloc,
     decode_workspace_bytes,
     kv_append,
     kv_bytes_per_token,

@@ -109,6 +109,8 @@ def _load() -> ctypes.CDLL:
                                                vp, c_sz, vp]),
         "kvc_decode_append_attention": (c_int, [P, vp, vp, vp, c_i32, c_i32, vp, c_i32, vp, c_i32,
                                                 fl, vp, vp, c_sz, vp]),
+        "kvc_decode_append_attention_noalloc": (c_int, [P, vp, vp, vp, c_i32, c_i32, vp, c_i32, vp,
+                                                        c_i32, fl, vp, vp]),
         "kvc_chunked_prefill_attention": (c_int, [P, vp, vp, vp, c_i32, vp, vp, c_i32, c_i32, vp,
                                                   c_i32, c_i32, fl, vp, vp]),
         "kvc_prefill_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
@@ -278,7 +280,7 @@ def decode_workspace_bytes(B: int, Hq: int, head_dim: int, max_context_len: int)
 
 
 def _decode(cache, q, k_new, v_new, block_table, context_lens, max_context_len, softmax_scale,
-            out, workspace):
+            out, workspace, noalloc=False):
     dev = cache.k_cache.device
     _need(q, "q", cache.dtype, 3, dev)
     _need(block_table, "block_table", torch.int32, 2, dev)
@@ -292,10 +294,19 @@ def _decode(cache, q, k_new, v_new, block_table, context_lens, max_context_len, 
             if t.shape != (B, cache.num_kv_heads, D):
                 raise ValueError(f"{n} must be [{B}, {cache.num_kv_heads}, {D}]")
     if out is None:
+        if noalloc:
+            raise ValueError("out is required (this call allocates nothing)")
         out = torch.empty_like(q)
     _need(out, "out", cache.dtype, 3, dev)
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
+    if noalloc:
+        scale = (1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
+        _check("kvc_decode_append_attention_noalloc", LIB.kvc_decode_append_attention_noalloc(
+            cache.c, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), B, Hq,
+            block_table.data_ptr(), block_table.shape[1], context_lens.data_ptr(),
+            int(max_context_len), scale, out.data_ptr(), _stream()))
+        return out
     need = decode_workspace_bytes(B, Hq, D, max_context_len)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -333,6 +344,20 @@ def decode_append_attention(cache: PagedKVCache, q: torch.Tensor, k_new: torch.T
     """One fused decode step: append k_new/v_new at position context_lens[b]-1, then attend."""
     return _decode(cache, q, k_new, v_new, block_table, context_lens, max_context_len,
                    softmax_scale, out, workspace)
+
+
+def decode_append_attention_noalloc(cache: PagedKVCache, q: torch.Tensor, k_new: torch.Tensor,
+                                    v_new: torch.Tensor, block_table: torch.Tensor,
+                                    context_lens: torch.Tensor, max_context_len: int,
+                                    out: torch.Tensor,
+                                    softmax_scale: float | None = None) -> torch.Tensor:
+    """decode_append_attention with no workspace and no allocation, for callers
+    that cannot allocate (kvc_decode_append_attention_noalloc: the split-K
+    partials use the library's per-device scratch array). ``out`` is required."""
+    if k_new is None or v_new is None:
+        raise ValueError("k_new and v_new are required")
+    return _decode(cache, q, k_new, v_new, block_table, context_lens, max_context_len,
+                   softmax_scale, out, None, noalloc=True)
 
 
 def prefill_workspace_bytes(n_seqs: int, total_tokens: int, max_chunk_len: int,

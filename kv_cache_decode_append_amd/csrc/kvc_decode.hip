@@ -2,6 +2,8 @@
 // the decode kernel (one 4-wave workgroup per work item, see kvc_decode_item.h
 // for the item), the merge kernel and the host entry points.
 
+#include <atomic>
+
 #include "kvc_decode_item.h"
 #include "kvc_host.h"
 
@@ -154,10 +156,34 @@ extern "C" size_t kvc_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head
 
 namespace kvc {
 
+// Split-K partials of kvc_decode_append_attention_noalloc: one array per
+// device, held until the process ends. Host code never passes this name to a
+// kernel (on the host it is only a stand-in for the symbol): it uses the
+// device address scratch_ptr() returns.
+static __device__ __align__(256) uint8_t scratch[KVC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current; nullptr if the runtime cannot give it. Calls from
+// several host threads may race to fill an entry, with the same value.
+static void* scratch_ptr() {
+  static std::atomic<void*> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = cached[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    cached[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+// use_scratch: the split-K partials go to `scratch` (workspace ignored), and a
+// call needing more than KVC_SCRATCH_BYTES is rejected with KVC_ERR_SCRATCH.
 static int decode_entry(const kvc_cache* cache, const void* q, const void* k_new, const void* v_new,
                         int32_t B, int32_t Hq, const int32_t* block_table, int32_t max_blocks,
                         const int32_t* context_lens, int32_t max_context_len, float softmax_scale,
-                        void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                        void* out, void* workspace, size_t workspace_bytes, void* stream,
+                        bool use_scratch = false) {
   int st = check_cache(cache);
   if (st != KVC_OK) return st;
   if (B < 0 || Hq <= 0 || max_blocks < 0 || max_context_len < 0) return KVC_ERR_SHAPE;
@@ -170,7 +196,9 @@ static int decode_entry(const kvc_cache* cache, const void* q, const void* k_new
 
   // the workspace rule is the size query's (it covers the most partitions
   // any device would use), so validation does not depend on the device
-  const size_t ws_rule = kvc_decode_workspace_bytes(B, Hq, cache->head_dim, max_context_len);
+  if (use_scratch) workspace = nullptr;
+  const size_t ws_rule =
+      use_scratch ? 0 : kvc_decode_workspace_bytes(B, Hq, cache->head_dim, max_context_len);
   if (ws_rule > 0 && (!workspace || workspace_bytes < ws_rule)) return KVC_ERR_WORKSPACE;
   if (!cache_aligned(cache) || !all_aligned(16, q, k_new, v_new, out, workspace) ||
       !all_aligned(4, block_table, context_lens))
@@ -183,7 +211,12 @@ static int decode_entry(const kvc_cache* cache, const void* q, const void* k_new
   const int n_part = nblk_max > 0 ? (int)ceil_div(nblk_max, pb) : 1;
   const size_t n_rows = (size_t)B * Hq * n_part;
   const size_t need = n_part > 1 ? n_rows * ((size_t)cache->head_dim * 4 + 8) : 0;
-  if (need > ws_rule) return KVC_ERR_WORKSPACE;   // cannot happen: pb >= kMinPartBlocks
+  if (use_scratch) {
+    if (need > KVC_SCRATCH_BYTES) return KVC_ERR_SCRATCH;
+    if (need > 0 && (workspace = scratch_ptr()) == nullptr) return KVC_ERR_LAUNCH;
+  } else if (need > ws_rule) {
+    return KVC_ERR_WORKSPACE;   // cannot happen: pb >= kMinPartBlocks
+  }
 
   DecodeArgs a;
   a.q = q;
@@ -232,4 +265,15 @@ extern "C" int kvc_decode_append_attention(const kvc_cache* cache, const void* q
   if (B > 0 && (!k_new || !v_new)) return KVC_ERR_NULL;
   return kvc::decode_entry(cache, q, k_new, v_new, B, Hq, block_table, max_blocks, context_lens,
                            max_context_len, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int kvc_decode_append_attention_noalloc(const kvc_cache* cache, const void* q,
+                                                   const void* k_new, const void* v_new, int32_t B,
+                                                   int32_t Hq, const int32_t* block_table,
+                                                   int32_t max_blocks, const int32_t* context_lens,
+                                                   int32_t max_context_len, float softmax_scale,
+                                                   void* out, void* stream) {
+  if (B > 0 && (!k_new || !v_new)) return KVC_ERR_NULL;
+  return kvc::decode_entry(cache, q, k_new, v_new, B, Hq, block_table, max_blocks, context_lens,
+                           max_context_len, softmax_scale, out, nullptr, 0, stream, true);
 }

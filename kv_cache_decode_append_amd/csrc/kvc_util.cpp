@@ -24,6 +24,7 @@ extern "C" const char* kvc_status_string(int status) {
     case KVC_ERR_STATE: return "block not held, out of range, or cached under another prefix";
     case KVC_ERR_NO_MEMORY: return "host memory ran out";
     case KVC_ERR_ALIGN: return "pointer not aligned as required (16 bytes for tensors and pools)";
+    case KVC_ERR_SCRATCH: return "call needs more than the built-in scratch (KVC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
