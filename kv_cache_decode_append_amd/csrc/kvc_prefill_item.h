@@ -116,12 +116,14 @@ struct PfShape {
   static constexpr int VCH = BF16 ? 2 : 1;          // chunks per V unit
   static constexpr int K_LDS = kKeyTile * RB;
   static constexpr int V_LDS = BF16 ? D * VT_STRIDE * 2 : kKeyTile * RB;
-  // bf16 tiles of 64 and 128 dims are staged by buffer->LDS loads into three
-  // K and three V buffers, both row-major with the chunk swizzle; the others
-  // go through registers into two K and two (transposed) V buffers
+  // bf16 tiles of 64 and 128 dims are staged by buffer->LDS loads into NBUF
+  // K and NBUF V buffers, both row-major with a chunk swizzle; the others go
+  // through registers into two K and two (transposed) V buffers
   static constexpr bool DMA_OK = BF16 && NC >= 8;
+  static constexpr int NBUF = 4;
+  static constexpr int BPB = 16 * RB / 1024;        // 1 KB staging loads per 16-token block
   static constexpr int TILES_REG = 2 * K_LDS + 2 * V_LDS;
-  static constexpr int TILES_DMA = DMA_OK ? 6 * K_LDS : 0;
+  static constexpr int TILES_DMA = DMA_OK ? 2 * NBUF * K_LDS : 0;
   static constexpr int TILES = TILES_REG > TILES_DMA ? TILES_REG : TILES_DMA;
   // pool rows of the blocks a workgroup reads, kept in LDS: 8,192 blocks
   // (131,072 keys) where the tile buffers leave room, else 2,048
@@ -341,47 +343,26 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
   };
   auto zero_unless = [](bool ok, const u32x4& v) { return ok ? v : u32x4{0u, 0u, 0u, 0u}; };
 
-  // Buffer->LDS staging: NC/W loads of 1 KB per wave and tile for each of K
-  // and V (W = kPfWaves). Load j of wave w fills rows (w + Wj) * 64/NC .. of
-  // the tile; lane l writes the 16-byte slot l % NC of row l / NC, so it
-  // fetches chunk (l % NC) ^ (key % NC) of that key (the swizzle every LDS
-  // reader expects).
-  static_assert(!DMA || S::NC % kPfWaves == 0, "whole 1 KB loads per wave");
-  constexpr int kDmaPerWave = DMA ? S::NC / kPfWaves : 1;
+  // Buffer->LDS staging (bf16, head dim 64 and 128): tiles go from the pool
+  // straight into LDS, 1 KB per wave instruction (64 / NC keys), lane l writing
+  // the 16-byte slot l % NC of its key's row. K rows hold chunk c at slot
+  // c ^ (key % NC), which makes the K fragment reads (16 keys x one chunk per
+  // 16 lanes) conflict-free. V rows are read by the transposing reads instead,
+  // whose 16 lanes take two adjacent chunks of four consecutive keys: with the
+  // K swizzle keys 2i and 2i + 1 put those chunks in the same banks, so V rows
+  // hold chunk c at slot c ^ 2 (key % (NC / 2)), which gives the rows of a read
+  // distinct banks. A lane fetches the chunk that belongs in its slot.
   constexpr int kKeysPerDma = 64 / S::NC;
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  uint32_t dma_voff[kDmaPerWave];
-  int dma_key[kDmaPerWave];
-  // V fragment read offsets inside a tile, per dim tile (see v_frag)
+  auto v_swz = [](int key) { return 2 * (key % (S::NC / 2)); };
+  // V fragment read offsets inside a tile, per dim tile (see v_frag_issue)
   int v_off[S::DT];
   if constexpr (DMA) {
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) {
-      const int key = (wu + kPfWaves * j) * kKeysPerDma + lane / S::NC;
-      dma_key[j] = key;
-      dma_voff[j] = (uint32_t)((key & 15) * S::RB + (((lane % S::NC) ^ (key % S::NC)) << 4));
-    }
     const int v_row = 4 * g + (l16 >> 2);
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
-      v_off[dt] = v_row * S::RB + (((2 * dt + ((l16 & 3) >> 1)) ^ (v_row % S::NC)) << 4) + (l16 & 1) * 8;
+      v_off[dt] = v_row * S::RB + (((2 * dt + ((l16 & 3) >> 1)) ^ v_swz(v_row)) << 4) + (l16 & 1) * 8;
   }
-  // Tile kt of the pool (K or V) into LDS; keys past the sequence's and
-  // blocks that hold none read as zeros (the buffer range check).
-  auto dma_tile = [&](int kt, const uint8_t* pool, uint8_t* lds) {
-    const bool cached = 4 * (kt - t_begin) < S::BT_CACHE;
-    const bool edge = kt * kKeyTile + kKeyTile > kv_len;
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) {
-      const int inst = wu + kPfWaves * j;
-      const int r = __builtin_amdgcn_readfirstlane(block_row(kt * 4 + inst * kKeysPerDma / 16, cached));
-      const uint8_t* base = pool + (r >= 0 ? (int64_t)r * (16 * S::RB) : 0);
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, r >= 0 ? 16u * S::RB : 0u);
-      uint32_t voff = dma_voff[j];
-      if (edge && kt * kKeyTile + dma_key[j] >= kv_len) voff = kDmaPastEnd;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + inst * 1024), 16, voff, 0, 0, 0);
-    }
-  };
 
   // Register staging of K and V tiles. K runs two tiles ahead of V (QK^T of
   // tile k+1 is computed before PV of tile k), so each is loaded on its own.
@@ -749,58 +730,154 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
     for (int n = 0; n < kRowTiles; ++n) asm volatile("" : "+v"(l_run[n]));
   };
   if constexpr (DMA) {
-    // Three K and three V buffers, tile t in buffer (t - t_begin) % 3.
-    // Iteration kt issues K(kt+3) and V(kt+2) into the buffers freed by the
-    // previous iteration, computes QK^T(kt+1) and PV(kt) + softmax(kt+1) as
-    // the register path does, then waits until K(kt+2) and V(kt+1) (issued
-    // one iteration earlier) have landed: every load has two iterations to
-    // arrive, and no tile passes through registers.
-    auto kb3 = [&](int b) { return smem + b * S::K_LDS; };
-    auto vb3 = [&](int b) { return smem + (3 + b) * S::K_LDS; };
-    // this wave's last `pending` loads may stay in flight; its LDS reads are done
-    auto wait_barrier = [](int pending) {
-      if (pending >= 8)
-        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      else if (pending >= 4)
-        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      else if (pending >= 2)
-        asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      else if (pending >= 1)
-        asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // Two groups of four waves with one wave of each on every SIMD (waves w
+    // and w + 4 share a SIMD). Each group alternates a matrix half-step
+    // (QK^T of tile k and PV of tile k - 1: 64 MFMAs, fragments from LDS)
+    // and a vector half-step (the softmax of tile k, the rescale, and its
+    // share of the tile staging), and group 1 runs one half-step behind
+    // group 0: on every SIMD one wave's MFMAs run while the other wave's
+    // vector work does. A workgroup barrier closes every half-step.
+    //   half-step 2k:   group 0 matrix(k),      group 1 vector(k - 1)
+    //   half-step 2k+1: group 0 vector(k),      group 1 matrix(k)
+    // K(k) and V(k) sit in buffer k % NB. Group 1 stages K tiles, group 0 V
+    // tiles, wave i of a group block i of the tile (16 keys). In vector(k)
+    // group 1 issues K(k + NB) (into the buffer K(k) left at half-step
+    // 2k + 1) and group 0 V(k + NB - 2) (V(k - 2) was last read at 2k - 1);
+    // at the end of every vector half-step a wave waits for its batch issued
+    // NB - 2 vector half-steps earlier, which the next matrix half-steps read
+    // (K(k + 2) from 2k + 4, V(k) from 2k + 2): every batch has NB - 2
+    // iterations to land.
+    constexpr int NB = S::NBUF;
+    constexpr int BPB = S::BPB;
+    const int grp = wu >> 2, wi = wu & 3;
+    const int n_t = t_end - t_begin;
+    auto kbuf = [&](int k) { return smem + (k % NB) * S::K_LDS; };
+    auto vbuf = [&](int k) { return smem + (NB + k % NB) * S::K_LDS; };
+    // lane l of load j writes the 16-byte slot l % NC of key j * 64/NC + l / NC
+    // of the block, so it fetches the chunk the tile's swizzle puts there
+    uint32_t blk_voff[BPB];
+#pragma unroll
+    for (int j = 0; j < BPB; ++j) {
+      const int kb = j * kKeysPerDma + lane / S::NC, key = wi * 16 + kb;
+      const int swz = grp == 1 ? key % S::NC : v_swz(key);   // group 1 stages K, group 0 V
+      blk_voff[j] = (uint32_t)(kb * S::RB + (((lane % S::NC) ^ swz) << 4));
+    }
+    // block wi of tile k of `pool` into `lds`; keys past the sequence and
+    // blocks that hold none read as zeros (the buffer range check)
+    auto stage = [&](int k, const uint8_t* pool, uint8_t* lds) {
+      const int kt = t_begin + k;
+      const int r = __builtin_amdgcn_readfirstlane(block_row(kt * 4 + wi, 4 * k < S::BT_CACHE));
+      const uint8_t* base = pool + (r >= 0 ? (int64_t)r * (16 * S::RB) : 0);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, r >= 0 ? 16u * S::RB : 0u);
+      const int key0 = kt * kKeyTile + wi * 16;
+      const bool edge = key0 + 16 > kv_len;
+#pragma unroll
+      for (int j = 0; j < BPB; ++j) {
+        uint32_t voff = blk_voff[j];
+        if (edge && key0 + j * kKeysPerDma + lane / S::NC >= kv_len) voff = kDmaPastEnd;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (wi * BPB + j) * 1024), 16,
+                                                 voff, 0, 0, 0);
+      }
+    };
+    // end of a half-step: this wave's LDS reads are done and, if `wait`, at
+    // most `newer` of its staging batches are still in flight; then the barrier
+    static_assert(NB >= 3 && NB <= 4, "newer batches: 0 .. 2");
+    auto half_step_end = [](bool wait, int newer) {
+      if (!wait)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (newer >= 2)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * S::BPB) : "memory");
+      else if (newer == 1)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(S::BPB) : "memory");
       else
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
-    const bool has1 = t_begin + 1 < t_end, has2 = t_begin + 2 < t_end;
-    dma_tile(t_begin, kbase, kb3(0));
-    dma_tile(t_begin, vbase, vb3(0));
-    if (has1) {
-      dma_tile(t_begin + 1, kbase, kb3(1));
-      dma_tile(t_begin + 1, vbase, vb3(1));
-    }
-    if (has2) dma_tile(t_begin + 2, kbase, kb3(2));
-    // K(t_begin), V(t_begin), K(t_begin + 1) landed
-    wait_barrier((has1 ? kDmaPerWave : 0) + (has2 ? kDmaPerWave : 0));
-    qk(kb3(0), sacc);
-    mask(sacc, t_begin * kKeyTile);
-    softmax(sacc, pt, alpha);                         // o is still zero: no rescale
-    lds_barrier();                                     // K(t_begin) read by every wave
-    int b0 = 0;                                        // buffer of tile kt
-    for (int kt = t_begin; kt + 1 < t_end; ++kt) {
-      const int b1 = b0 == 2 ? 0 : b0 + 1, b2 = b1 == 2 ? 0 : b1 + 1;
-      const bool k3 = kt + 3 < t_end, v2 = kt + 2 < t_end;
-      if (k3) dma_tile(kt + 3, kbase, kb3(b0));        // K(kt) was read last iteration
-      if (v2) dma_tile(kt + 2, vbase, vb3(b2));        // V(kt-1) likewise
-      qk(kb3(b1), sacc);
-      mask(sacc, (kt + 1) * kKeyTile);
-      PTile pt_next;
-      pv_softmax(vb3(b0), pt, sacc, pt_next, alpha);
-      pin(pt_next);
+    // staging batches a wave issued after the one it waits for at the end of
+    // vector(k): K(k + 3 .. k + NB) for group 1 (it waits for K(k + 2)),
+    // V(k + 1 .. k + NB - 2) for group 0 (it waits for V(k)); k = -1: the prologue
+    auto newer_batches = [&](int k) {
+      const int first = grp == 1 ? k + 3 : k + 1, last = grp == 1 ? k + NB : k + NB - 2;
+      return max(0, min(last, n_t - 1) - first + 1);
+    };
+    // matrix half-step: QK^T of tile k (QK) and PV of tile k - 1 (PV), one
+    // QK^T step and one PV step at a time (each both row tiles), K fragments
+    // read three steps ahead and V fragments two
+    auto matrix = [&](auto qk_tag, auto pv_tag, int k) {
+      constexpr bool QK = decltype(qk_tag)::value, PV = decltype(pv_tag)::value;
+      constexpr int kQ = 4 * S::KS, kP = 2 * S::DT;      // steps of each product
+      constexpr int kSteps = QK ? kQ : kP;
+      static_assert(!QK || !PV || kQ == kP, "the two products interleave step for step");
+      const uint8_t* kl = kbuf(k);
+      const uint8_t* vl = vbuf(k + NB - 1);              // tile k - 1
+      bf16x8_t kf[4];
+      auto kfrag = [&](int st) {
+        const int key = (st / S::KS) * 16 + l16, c = (st % S::KS) * 4 + g;
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
+                                                kl + key * S::RB + ((c ^ (key % S::NC)) << 4)));
+      };
+      VHalves vf[3];
+      if constexpr (QK) {
+#pragma unroll
+        for (int st = 0; st < 3; ++st) kf[st] = kfrag(st);
+      }
+      if constexpr (PV) {
+        vf[0] = v_frag_issue(vl, 0, 0);
+        vf[1] = v_frag_issue(vl, 1 / S::DT, 1 % S::DT);
+      }
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        if constexpr (QK) {
+          if (st + 3 < kQ) kf[(st + 3) % 4] = kfrag(st + 3);
+          const int m = st / S::KS, kk = st % S::KS;
+#pragma unroll
+          for (int nn = 0; nn < kRowTiles; ++nn)
+            sacc[m][nn] = M::mma(kf[st % 4], qf[nn][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[m][nn]);
+        }
+        if constexpr (PV) {
+          if (st + 2 < kP) vf[(st + 2) % 3] = v_frag_issue(vl, (st + 2) / S::DT, (st + 2) % S::DT);
+          const int newer = kP - 1 - st < 2 ? kP - 1 - st : 2;
+          const bf16x8_t va = v_frag_use(vf[st % 3], newer);
+          const int mp = st / S::DT, dt = st % S::DT;
+#pragma unroll
+          for (int nn = 0; nn < kRowTiles; ++nn)
+            o[nn][dt] = M::mma(va, __builtin_bit_cast(bf16x8_t, pt.v[mp][nn]), o[nn][dt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // vector half-step: softmax of tile k, the rescale of the accumulators,
+    // this wave's staging batch and the wait for its older one
+    auto vector = [&](int k) {
+      mask(sacc, (t_begin + k) * kKeyTile);
+      softmax(sacc, pt, alpha);
       rescale(alpha);
-      pt = pt_next;
-      wait_barrier(((int)k3 + (int)v2) * kDmaPerWave);  // K(kt+2), V(kt+1) landed
-      b0 = b1;
+      // one call site, its pool, buffer and tile chosen by selects (two call
+      // sites, one per group, were merged by the compiler into a block that
+      // left the K pool's base unset on group 1's path)
+      const int ks = grp == 1 ? k + NB : k + NB - 2;
+      if (ks < n_t) stage(ks, grp == 1 ? kbase : vbase, grp == 1 ? kbuf(ks) : vbuf(ks));
+      half_step_end(true, newer_batches(k));
+    };
+
+    // prologue: K(0 .. NB-1) by group 1, V(0 .. NB-3) by group 0; K(0) and
+    // K(1) must have landed before the first matrix half-steps
+    {
+      const int n_pro = min(grp == 1 ? NB : NB - 2, n_t);
+      for (int k = 0; k < n_pro; ++k) stage(k, grp == 1 ? kbase : vbase, grp == 1 ? kbuf(k) : vbuf(k));
+      half_step_end(grp == 1, newer_batches(-1));      // group 1: K(2 .. NB-1) may stay in flight
     }
-    pv(vb3(b0), pt);
+    if (grp == 1) half_step_end(false, 0);            // half-step 0: group 1 idle
+    matrix(std::true_type{}, std::false_type{}, 0);
+    half_step_end(false, 0);
+    vector(0);
+    for (int k = 1; k < n_t; ++k) {
+      matrix(std::true_type{}, std::true_type{}, k);
+      half_step_end(false, 0);
+      vector(k);
+    }
+    matrix(std::false_type{}, std::true_type{}, n_t);
+    half_step_end(false, 0);
+    if (grp == 0) half_step_end(false, 0);            // last half-step: group 0 idle
   } else {
   auto kbuf = [&](int i) { return smem + (i & 1) * S::K_LDS; };
   auto vbuf = [&](int i) { return smem + 2 * S::K_LDS + (i & 1) * S::V_LDS; };
