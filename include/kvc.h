@@ -129,7 +129,12 @@ int64_t kvc_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_di
                                int32_t dtype_bytes);
 
 /* Slot of each new token: slot[t] = block_table[seq_ids[t]][p / bs] * bs + p % bs
- * with p = positions[t]; p < 0 gives slot -1 (a padding token).
+ * with p = positions[t]; p < 0 gives slot -1 (a padding token). The cache is a
+ * pool of fixed 16-token blocks that each sequence reaches through its own block
+ * table (daviddominguez.dev "The KV cache and prefix caching", sections "What
+ * prefill stores and decode reads" (PagedAttention) and "A prefix already in
+ * the cache can skip its prefill" (16-token blocks)); the slot is where
+ * position p of that sequence lives in the pool.
  *   block_table  device int32 [n_seqs][max_blocks] (row-major)
  *   seq_ids      device int32 [T], row of block_table for each token; a row
  *                outside [0, n_seqs) gives slot -1 and KVC_DEVERR_CONTEXT
@@ -144,7 +149,11 @@ int kvc_slot_mapping(const int32_t* block_table, int32_t n_seqs, int32_t max_blo
                      int32_t block_size, int64_t* slot_mapping, int32_t* err_flag,
                      void* stream);
 
-/* Append: k_cache[slot / bs][h][slot % bs][:] = k[t][h][:], same for v.
+/* Append: k_cache[slot / bs][h][slot % bs][:] = k[t][h][:], same for v. Each
+ * step stores the new position's key and value once, and later steps only read
+ * them (aiwithghost.com "KV cache and continuous batching: 1,000 people ask AI",
+ * section "What does a KV cache keep?"; daviddominguez.dev, section "What
+ * prefill stores and decode reads").
  *   k, v          device [T][num_kv_heads][head_dim], cache dtype (no conversion:
  *                 the cache contents are bit-exact copies); bf16 for a KVC_FP8
  *                 cache, whose rows are quantised as the header describes
@@ -159,7 +168,12 @@ int kvc_kv_append(const kvc_cache* cache, const int64_t* slot_mapping, const voi
 size_t kvc_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim,
                                   int32_t max_context_len);
 
-/* Paged GQA decode attention for a batch of sequences of mixed lengths.
+/* Paged GQA decode attention for a batch of sequences of mixed lengths: each
+ * sequence's newest query attends over every key and value its cache holds,
+ * read through its block table, with Hq / Hkv query heads sharing each K/V head
+ * (aiwithghost.com, section "What does a KV cache keep?"; daviddominguez.dev,
+ * sections "What prefill stores and decode reads" and "The prompt is paid
+ * once, the output is paid every step").
  *   q             device [B][Hq][head_dim], cache dtype (bf16 for KVC_FP8): each
  *                 sequence's newest query
  *   block_table   device int32 [B][max_blocks]
@@ -221,7 +235,13 @@ int kvc_decode_append_attention_noalloc(const kvc_cache* cache, const void* q, c
 
 /* Chunked prefill: write a prompt chunk's K/V into the cache, then causal
  * attention of each chunk position over the cached prefix plus the chunk's
- * positions up to and including itself.
+ * positions up to and including itself. Prompts run in chunks of a token
+ * budget so decode rows wait at most one chunk (gouthm.com "The KV cache is not
+ * your bottleneck", section "The fix that mattered"), a chunk can start after
+ * a prefix already cached (daviddominguez.dev, section "A prefix already in
+ * the cache can skip its prefill"), and the prompt's positions are processed
+ * together as matrix products (aiwithghost.com, section "What does a KV cache
+ * keep?").
  *   q             device [total_tokens][Hq][head_dim], chunks of all sequences
  *                 packed back to back
  *   k, v          device [total_tokens][num_kv_heads][head_dim]: the chunk's K/V
