@@ -135,6 +135,37 @@ def generate_cached(q, k, v, prompt: int, answer: int, scale: float):
     return np.stack(outs), kv_rows, (cache_k, cache_v)
 
 
+def attend_positions(q_rows, k_seq, v_seq, positions, scale: float) -> np.ndarray:
+    """Query rows of one sequence at absolute positions `positions`, each over
+    keys 0 .. its position (the causal window of attend_row), computed for all
+    rows of a query head at once: logits scale * Q K^T, keys past a row's
+    position removed, row-wise softmax, then weights times V. The same
+    definition as attend_row in matrix form, for checking many rows over long
+    prefixes (a whole query tile or chunk).
+
+    q_rows: [R, Hq, D]; k_seq, v_seq: [>= max(positions) + 1, Hkv, D];
+    positions: [R] ints. Returns [R, Hq, D] in fp64.
+    """
+    q = np.asarray(q_rows, dtype=np.float64)
+    pos = np.asarray(positions, dtype=np.int64)
+    n = int(pos.max()) + 1
+    k = np.asarray(k_seq[:n], dtype=np.float64)
+    v = np.asarray(v_seq[:n], dtype=np.float64)
+    r, hq, d = q.shape
+    hkv = k.shape[1]
+    assert pos.shape == (r,) and pos.min() >= 0 and hq % hkv == 0 and k.shape[2] == d
+    group = hq // hkv
+    outside = np.arange(n)[None, :] > pos[:, None]            # [R, n] keys a row may not see
+    out = np.empty((r, hq, d), dtype=np.float64)
+    for h in range(hq):
+        g = h // group
+        s = scale * (q[:, h, :] @ k[:, g, :].T)                 # [R, n] logits
+        s[outside] = -np.inf
+        p = np.exp(s - s.max(axis=1, keepdims=True))           # unnormalised weights
+        out[:, h, :] = (p @ v[:, g, :]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
 def decode_rows(q_new, k_seqs, v_seqs, scale: float) -> np.ndarray:
     """One decode step for a batch of sequences of mixed lengths.
 

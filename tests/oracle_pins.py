@@ -142,6 +142,26 @@ def prefill_err_vs_sdpa(prefill_chunk_rows, seed=6) -> float:
     return worst
 
 
+def positions_err_vs_sdpa(attend_positions, seed=9) -> float:
+    """Rows at given positions (a whole chunk, and a scattered subset of one)
+    against torch SDPA with the bottom-right causal mask."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for hkv, g, d, prefix, c in [(2, 4, 32, 0, 7), (1, 2, 16, 17, 16), (2, 1, 64, 33, 5),
+                                 (1, 4, 16, 40, 1), (2, 4, 16, 90, 40)]:
+        hq = hkv * g
+        q = _rand(rng, c, hq, d)
+        k, v = _rand(rng, prefix + c, hkv, d), _rand(rng, prefix + c, hkv, d)
+        scale = 1.0 / math.sqrt(d)
+        ref = sdpa_causal_rows(q, k, v, prefix, scale)
+        got = attend_positions(q, k, v, prefix + np.arange(c), scale)
+        worst = max(worst, float(np.max(np.abs(got - ref))))
+        sub = np.sort(rng.choice(c, size=max(1, c // 3), replace=False))
+        got = attend_positions(q[sub], k, v, prefix + sub, scale)
+        worst = max(worst, float(np.max(np.abs(got - ref[sub]))))
+    return worst
+
+
 # ---------------------------------------------------------------- paged pins
 def golden_slots_ok(slot_of) -> bool:
     with open(os.path.join(GOLD, "paged_example.json")) as f:

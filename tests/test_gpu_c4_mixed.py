@@ -108,6 +108,15 @@ def test_c4_skewed_mixed_step(kvc):
         ref = np.stack([OA.attend_row(oracle_values(q[r], "bf16"), oracle_values(k[:p0 + r + 1], "bf16"),
                                       oracle_values(v[:p0 + r + 1], "bf16"), scale) for r in rows])
         assert_close(got_pre[i * chunk + np.array(rows)], ref, "bf16", f"C4 prefill row {b}")
+    # every row and head of the whole chunk of the shortest prefill row (matrix-form oracle)
+    i = int(np.argmin(ctx[pre_rows]))
+    b = int(pre_rows[i])
+    k, v, q = vals[b]
+    p0 = int(ctx[b]) - chunk
+    say(f"C4 prefill row {b}: all {chunk} rows over a {p0}-token prefix")
+    ref = OA.attend_positions(oracle_values(q, "bf16"), oracle_values(k, "bf16"),
+                              oracle_values(v, "bf16"), p0 + np.arange(chunk), scale)
+    assert_close(got_pre[i * chunk:(i + 1) * chunk], ref, "bf16", f"C4 prefill row {b}, whole chunk")
     # the appended tokens and the prefill chunks landed at their slots (bitwise)
     kb = device_bits(cache.k_cache)
     for b in exact:

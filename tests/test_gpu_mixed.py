@@ -203,6 +203,30 @@ def test_workspace_is_reused_and_left_clean(kvc):
         assert int(ws[:256].count_nonzero().item()) == 0, "queue header not reset"
 
 
+def test_phase0_wait_gives_up_on_a_corrupt_header(kvc):
+    """The wait for the first phase is bounded: with the workspace header's
+    finished-items counter set so that it can never reach the phase-0 item
+    count (a corrupt header, forced from the host), every waiting workgroup
+    gives up after its spin limit, the call flags KVC_DEVERR_QUEUE and every
+    workgroup still exits; the last one out leaves the header zero, and the
+    next call on the same workspace is right again."""
+    case = MixedCase("mixed-giveup", 424, 16, 4, 64, "bf16", [40, 300], [10, 0], [50, 70])
+    need = kvc.mixed_workspace_bytes(case.n_dec, max(case.dec_ctx), 16, 4, 64)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    hdr = ws[:12].view(torch.int32)                    # next item, phase-0 items done, exited
+    hdr[1] = -1000
+    say("mixed step with a corrupt queue header: the phase-0 wait must give up")
+    cache = case.fill(kvc)
+    kvc.mixed_step_attention(cache, case.w.Hq, workspace=ws, **case.inputs())
+    torch.cuda.synchronize()
+    assert int(cache.err_flag.item()) & kvc.DEVERR_QUEUE
+    assert int(ws[:256].count_nonzero().item()) == 0, "queue header not reset"
+    cache.err_flag.zero_()
+    out_dec, out_pf = kvc.mixed_step_attention(cache, case.w.Hq, workspace=ws, **case.inputs())
+    torch.cuda.synchronize()
+    case.check(cache, out_dec, out_pf)
+
+
 def test_c4_skewed_step_in_one_launch(kvc):
     """The skewed continuous-batching step at full size (206 decode rows with
     lognormal contexts up to 32,000, 4 rows with a 2,048-token chunk), in the
@@ -282,6 +306,15 @@ def test_c4_skewed_step_in_one_launch(kvc):
                                       oracle_values(k[:p0 + r + 1], "bf16"),
                                       oracle_values(v[:p0 + r + 1], "bf16"), scale) for r in rows])
         assert_close(got[i * chunk + np.array(rows)], ref, "bf16", f"C4 prefill row {b}")
+    # every row and head of the whole chunk of the shortest prefill row (matrix-form oracle)
+    i = int(np.argmin(ctx[pre_rows]))
+    b = int(pre_rows[i])
+    k, v, q = vals[b]
+    p0 = int(ctx[b]) - chunk
+    say(f"C4 prefill row {b}: all {chunk} rows over a {p0}-token prefix")
+    ref = OA.attend_positions(oracle_values(q, "bf16"), oracle_values(k, "bf16"),
+                              oracle_values(v, "bf16"), p0 + np.arange(chunk), scale)
+    assert_close(got[i * chunk:(i + 1) * chunk], ref, "bf16", f"C4 prefill row {b}, whole chunk")
     kb = device_bits(cache.k_cache)
     for b in exact:
         k = vals[b][0]

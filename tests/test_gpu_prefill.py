@@ -107,7 +107,19 @@ def test_c5_prefill_chunk_over_long_prefix(kvc):
 
     def rows(i):
         return sorted(set([0, 1, 15, 16, 1023, 2047] + rng.integers(0, W.C5_CHUNK, 4).tolist()))
-    cache, _ = _check(kvc, case, "C5 prefill", pool=False, rows=rows)
+    cache, out = _check(kvc, case, "C5 prefill", pool=False, rows=rows)
+    # every row and head of sequence 0's first and last query tile (the last holds
+    # the causal diagonal), against the matrix-form oracle
+    from oracle import attention as OA
+    from tests.gpu_cases import oracle_values
+    mp = 256 // (W.C5.Hq // W.C5.Hkv)               # positions per query tile
+    got = out.float().cpu().numpy()[case.cu[0]:case.cu[1]]
+    kq, vq = oracle_values(case.k[0], "bf16"), oracle_values(case.v[0], "bf16")
+    for lo in (0, W.C5_CHUNK - mp):
+        r = np.arange(lo, lo + mp)
+        ref = OA.attend_positions(oracle_values(case.q[0][r], "bf16"), kq, vq, W.C5_PREFIX + r,
+                                  OA.default_scale(W.C5.D))
+        assert_close(got[r], ref, "bf16", f"C5 seq 0 query tile at {lo}, every row and head")
     # the chunk's K/V landed at their slots (sampled tokens, bitwise)
     from oracle import paged as OP
     from tests.gpu_cases import oracle_bits

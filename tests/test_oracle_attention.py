@@ -43,6 +43,10 @@ def test_prefill_rows_match_sdpa_with_offset_mask():
     assert P.prefill_err_vs_sdpa(A.prefill_chunk_rows) < 1e-12
 
 
+def test_position_rows_match_sdpa_with_offset_mask():
+    assert P.positions_err_vs_sdpa(A.attend_positions) < 1e-12
+
+
 def test_paged_golden_slots():
     assert P.golden_slots_ok(paged.slot_of)
 

@@ -96,3 +96,31 @@ def test_slot_off_by_one_block_is_caught():
 
         gather = staticmethod(paged.gather)
     assert not P.gather_scatter_roundtrip(Bad)
+
+
+def _positions(q_rows, k_seq, v_seq, positions, scale, *, reach=0, head_map=None):
+    """attend_positions with a planted slip: the window ends `reach` keys off, or
+    the query head reads another kv head."""
+    q = np.asarray(q_rows, np.float64)
+    pos = np.asarray(positions)
+    n = int(pos.max()) + 1
+    k, v = np.asarray(k_seq[:n], np.float64), np.asarray(v_seq[:n], np.float64)
+    hq, hkv = q.shape[1], k.shape[1]
+    out = np.empty(q.shape)
+    for h in range(hq):
+        g = (h // (hq // hkv)) if head_map is None else head_map(h, hkv)
+        s = scale * (q[:, h, :] @ k[:, g, :].T)
+        s[np.arange(n)[None, :] > pos[:, None] + reach] = -np.inf
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        out[:, h, :] = (p @ v[:, g, :]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+@pytest.mark.parametrize("kw", [dict(reach=-1), dict(reach=1), dict(head_map=lambda h, hkv: h % hkv)])
+def test_position_rows_mutant_is_caught(kw):
+    with np.errstate(all="ignore"):
+        assert not P.positions_err_vs_sdpa(lambda *a: _positions(*a, **kw)) < 1e-12
+
+
+def test_position_rows_unmutated_copy_passes():
+    assert P.positions_err_vs_sdpa(_positions) < 1e-12
