@@ -220,6 +220,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
   // their partial dot products with one DPP step.
   const int h = lane / S::LPH, qh = (lane % S::LPH) % S::QS, tt = (lane % S::LPH) / S::QS;
   const bool active = h < G;
+  // QK token of the lane's sub-step sl (the lanes of one sub-step read rows
+  // 0 .. TPS-1 of a group apart, which keeps the swizzled K reads
+  // conflict-free)
+  auto tok = [&](int sl) { return tt + S::TPS * sl; };
   u32x4 qv[S::NCQ];
   {
     const int hq = kvh * G + (active ? h : 0);
@@ -281,8 +285,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     for (int j = 0; j < S::NI; ++j) vb[j] = buffer_load16_stream(rv, (uint32_t)(j * 64 + lane) * 16u);
   };
   // fp8: the codes of the same (token, 8 values) each bf16 load would hold,
-  // 8 bytes per lane, and the tile's row scales (lane l: token l % 16).
-  auto issue8 = [&](u32x2 (&kr)[S::NI], u32x2 (&vr)[S::NI], float& sk, float& sv, int i) {
+  // 8 bytes per lane, and the row scales of the lane's own QK tokens
+  // tok(0) .. tok(SPL - 1), each loaded by the lane itself, so that no lane
+  // has to fetch another's scale.
+  auto issue8 = [&](u32x2 (&kr)[S::NI], u32x2 (&vr)[S::NI], float (&sk)[S::SPL],
+                    float (&sv)[S::SPL], int i) {
     const int64_t tile = tile_of(i);
     const size_t off = tile >= 0 ? (size_t)tile * TILE_MEM : 0;
     const uint32_t bytes = tile >= 0 ? TILE_MEM : 0;
@@ -298,10 +305,12 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     for (int j = 0; j < S::NI; ++j)
       vr[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                                             rv, (uint32_t)(j * 64 + lane) * 8u, 0, kCachePolicyNonTemporal));
-    sk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, (uint32_t)(lane & 15) * 4u, 0,
-                                                               kCachePolicyNonTemporal));
-    sv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, (uint32_t)(lane & 15) * 4u, 0,
-                                                               kCachePolicyNonTemporal));
+#pragma unroll
+    for (int sl = 0; sl < S::SPL; ++sl) {
+      const uint32_t soff = (uint32_t)tok(sl) * 4u;
+      sk[sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, soff, 0, kCachePolicyNonTemporal));
+      sv[sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, soff, 0, kCachePolicyNonTemporal));
+    }
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -350,7 +359,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       }
     }
   };
-  float cur_sk = 0.f, cur_sv = 0.f;   // fp8: the block's row scales, lane l: token l % 16
+  float cur_sk[S::SPL], cur_sv[S::SPL];   // fp8: the row scales of the lane's QK tokens
   u32x2 cur_v8[S::NI];                 // fp8: the block's V codes (the same units as vb)
   // One block. TAIL marks the sequence's last block, the only one that can be
   // partial or hold the appended token; every other block skips the masking
@@ -383,7 +392,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     float s[S::SPL];
 #pragma unroll
     for (int sl = 0; sl < S::SPL; ++sl) {
-      const int t = tt + S::TPS * sl;
+      const int t = tok(sl);
       float part_s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cc = 0; cc < S::NCQ; ++cc) {
@@ -396,8 +405,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       const bool valid = active && (!TAIL || lb * 16 + t < ctx);
       if constexpr (F8) {
         // the key row's scale multiplies its dot product
-        const float skt = __int_as_float(__builtin_amdgcn_ds_bpermute(t * 4, __float_as_int(cur_sk)));
-        s[sl] = valid ? dot * skt * a.scale_log2 : -INFINITY;
+        s[sl] = valid ? dot * cur_sk[sl] * a.scale_log2 : -INFINITY;
       } else {
         s[sl] = valid ? dot * a.scale_log2 : -INFINITY;
       }
@@ -429,16 +437,14 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     for (int sl = 0; sl < S::SPL; ++sl) {
       pw[sl] = p[sl];
       if constexpr (F8) {
-        const int t = tt + S::TPS * sl;
-        const float svt = __int_as_float(__builtin_amdgcn_ds_bpermute(t * 4, __float_as_int(cur_sv)));
         // rows past the context may hold NaN scales; their weight is 0
-        pw[sl] = (!TAIL || lb * 16 + t < ctx) ? p[sl] * svt : 0.f;
+        pw[sl] = (!TAIL || lb * 16 + tok(sl) < ctx) ? p[sl] * cur_sv[sl] : 0.f;
       }
     }
     if (active && qh == 0) {
 #pragma unroll
       for (int sl = 0; sl < S::SPL; ++sl) {
-        const int t = tt + S::TPS * sl;
+        const int t = tok(sl);
         if constexpr (S::DOT2_PV) {
           // packed bf16 pairs in PV order: token t = j*TPI + r sits in pair
           // (j/2)*TPI + r, low half for even j
@@ -524,8 +530,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
   // fp8: convert a ring slot's K codes to the bf16 tile the shared path reads
   // and hand its V codes to the PV product as they are (with the new token's
   // codes and scales in place for the tail block), then process it.
-  auto process8 = [&](auto tail_tag, u32x2 (&kr)[S::NI], u32x2 (&vr)[S::NI], float sk, float sv,
-                      int i) {
+  auto process8 = [&](auto tail_tag, u32x2 (&kr)[S::NI], u32x2 (&vr)[S::NI],
+                      const float (&sk)[S::SPL], const float (&sv)[S::SPL], int i) {
     constexpr bool TAIL = decltype(tail_tag)::value;
     static_assert(S::DOT2_PV, "fp8 V codes go straight into the packed PV product");
     u32x4 kb[S::NI], vb[S::NI] = {};   // vb unused: PV reads the codes in cur_v8
@@ -541,12 +547,15 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       kb[j] = e4m3x8_to_bf16x8(kx);
       cur_v8[j] = vx;
     }
-    cur_sk = sk;
-    cur_sv = sv;
-    if constexpr (TAIL) {
-      if (fuse && (lane & 15) == t_new) {
-        cur_sk = k_new_s;
-        cur_sv = v_new_s;
+#pragma unroll
+    for (int sl = 0; sl < S::SPL; ++sl) {
+      cur_sk[sl] = sk[sl];
+      cur_sv[sl] = sv[sl];
+      if constexpr (TAIL) {
+        if (fuse && tok(sl) == t_new) {
+          cur_sk[sl] = k_new_s;
+          cur_sv[sl] = v_new_s;
+        }
       }
     }
     process(tail_tag, kb, vb, i);
@@ -557,22 +566,30 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     // Ring of PF blocks in flight; a slot is refilled right after it is used.
     // A wave's blocks ascend, so only its last step can be the sequence's last
     // block: the loop runs the plain path only and the last step is peeled.
+    // The loop takes whole turns of the ring only, and the few steps left
+    // before the last one follow it: with a step that may be skipped inside
+    // the loop, the loop head would have to assume that the refills after it
+    // were not made, and its waits for the oldest slot would drain the ring.
+    // (The steps after the loop need no refill: every index they would load
+    // lies past the wave's blocks.)
     const int n_main = n_my > 0 ? n_my - 1 : 0;
     if constexpr (F8) {
       u32x2 kr[PF][S::NI], vr[PF][S::NI];
-      float skr[PF], svr[PF];
+      float skr[PF][S::SPL], svr[PF][S::SPL];
 #pragma unroll
       for (int u = 0; u < PF; ++u) issue8(kr[u], vr[u], skr[u], svr[u], u);
-      for (int i = 0; i < n_main; i += PF) {
+      int i = 0;
+      for (; i + PF <= n_main; i += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
-          if (i + u < n_main) {
-            process8(std::false_type{}, kr[u], vr[u], skr[u], svr[u], i + u);
-            __builtin_amdgcn_sched_barrier(0);
-            issue8(kr[u], vr[u], skr[u], svr[u], i + u + PF);
-          }
+          process8(std::false_type{}, kr[u], vr[u], skr[u], svr[u], i + u);
+          __builtin_amdgcn_sched_barrier(0);
+          issue8(kr[u], vr[u], skr[u], svr[u], i + u + PF);
         }
       }
+#pragma unroll
+      for (int u = 0; u < PF - 1; ++u)
+        if (i + u < n_main) process8(std::false_type{}, kr[u], vr[u], skr[u], svr[u], i + u);
       if (n_my > 0) {
         const int last = n_my - 1, slot = last % PF;
         const bool tail = blk0 + w + last * NW == nblk - 1;
@@ -594,18 +611,20 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       u32x4 kb[S::PF][S::NI], vb[S::PF][S::NI];
 #pragma unroll
       for (int u = 0; u < S::PF; ++u) issue(kb[u], vb[u], u);
-      for (int i = 0; i < n_main; i += S::PF) {
+      int i = 0;
+      for (; i + S::PF <= n_main; i += S::PF) {
 #pragma unroll
         for (int u = 0; u < S::PF; ++u) {
-          if (i + u < n_main) {
-            process(std::false_type{}, kb[u], vb[u], i + u);
-            // keep the refill of this slot after its use: hoisting the loads
-            // above the PV products would force a register copy of the tile
-            __builtin_amdgcn_sched_barrier(0);
-            issue(kb[u], vb[u], i + u + S::PF);
-          }
+          process(std::false_type{}, kb[u], vb[u], i + u);
+          // keep the refill of this slot after its use: hoisting the loads
+          // above the PV products would force a register copy of the tile
+          __builtin_amdgcn_sched_barrier(0);
+          issue(kb[u], vb[u], i + u + S::PF);
         }
       }
+#pragma unroll
+      for (int u = 0; u < S::PF - 1; ++u)
+        if (i + u < n_main) process(std::false_type{}, kb[u], vb[u], i + u);
       if (n_my > 0) {
         const int last = n_my - 1, slot = last % S::PF;
         const bool tail = blk0 + w + last * NW == nblk - 1;
