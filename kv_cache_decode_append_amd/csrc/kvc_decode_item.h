@@ -394,11 +394,26 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     for (int sl = 0; sl < S::SPL; ++sl) {
       const int t = tok(sl);
       float part_s[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (F8) {
+        // all of the sub-step's K reads first: the fp8 wave is short of
+        // independent work to cover LDS latency (the bf16 wave is not, and
+        // keeps the registers)
+        u32x4 kk[S::NCQ];
 #pragma unroll
-      for (int cc = 0; cc < S::NCQ; ++cc) {
-        const int c = qh * S::NCQ + cc;
-        const u32x4 kk = *reinterpret_cast<const u32x4*>(kst + t * S::RB + ((c ^ (t % S::NC)) << 4));
-        chunk_dot<C>(kk, qv[cc], part_s);
+        for (int cc = 0; cc < S::NCQ; ++cc) {
+          const int c = qh * S::NCQ + cc;
+          kk[cc] = *reinterpret_cast<const u32x4*>(kst + t * S::RB + ((c ^ (t % S::NC)) << 4));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int cc = 0; cc < S::NCQ; ++cc) chunk_dot<C>(kk[cc], qv[cc], part_s);
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < S::NCQ; ++cc) {
+          const int c = qh * S::NCQ + cc;
+          const u32x4 kk = *reinterpret_cast<const u32x4*>(kst + t * S::RB + ((c ^ (t % S::NC)) << 4));
+          chunk_dot<C>(kk, qv[cc], part_s);
+        }
       }
       float dot = (part_s[0] + part_s[1]) + (part_s[2] + part_s[3]);
       dot += dpp_f<kQuadXor1>(dot);                  // the other half of the head dim
@@ -571,25 +586,39 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     // the loop, the loop head would have to assume that the refills after it
     // were not made, and its waits for the oldest slot would drain the ring.
     // (The steps after the loop need no refill: every index they would load
-    // lies past the wave's blocks.)
+    // lies past the wave's blocks.) The mixed kernel's whole-sequence item
+    // keeps guarded turns: it has no registers to spare for the extra steps.
     const int n_main = n_my > 0 ? n_my - 1 : 0;
     if constexpr (F8) {
       u32x2 kr[PF][S::NI], vr[PF][S::NI];
       float skr[PF][S::SPL], svr[PF][S::SPL];
 #pragma unroll
       for (int u = 0; u < PF; ++u) issue8(kr[u], vr[u], skr[u], svr[u], u);
-      int i = 0;
-      for (; i + PF <= n_main; i += PF) {
+      if constexpr (WHOLE) {
+        for (int i = 0; i < n_main; i += PF) {
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
-          process8(std::false_type{}, kr[u], vr[u], skr[u], svr[u], i + u);
-          __builtin_amdgcn_sched_barrier(0);
-          issue8(kr[u], vr[u], skr[u], svr[u], i + u + PF);
+          for (int u = 0; u < PF; ++u) {
+            if (i + u < n_main) {
+              process8(std::false_type{}, kr[u], vr[u], skr[u], svr[u], i + u);
+              __builtin_amdgcn_sched_barrier(0);
+              issue8(kr[u], vr[u], skr[u], svr[u], i + u + PF);
+            }
+          }
         }
-      }
+      } else {
+        int i = 0;
+        for (; i + PF <= n_main; i += PF) {
 #pragma unroll
-      for (int u = 0; u < PF - 1; ++u)
-        if (i + u < n_main) process8(std::false_type{}, kr[u], vr[u], skr[u], svr[u], i + u);
+          for (int u = 0; u < PF; ++u) {
+            process8(std::false_type{}, kr[u], vr[u], skr[u], svr[u], i + u);
+            __builtin_amdgcn_sched_barrier(0);
+            issue8(kr[u], vr[u], skr[u], svr[u], i + u + PF);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < PF - 1; ++u)
+          if (i + u < n_main) process8(std::false_type{}, kr[u], vr[u], skr[u], svr[u], i + u);
+      }
       if (n_my > 0) {
         const int last = n_my - 1, slot = last % PF;
         const bool tail = blk0 + w + last * NW == nblk - 1;
@@ -611,20 +640,33 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       u32x4 kb[S::PF][S::NI], vb[S::PF][S::NI];
 #pragma unroll
       for (int u = 0; u < S::PF; ++u) issue(kb[u], vb[u], u);
-      int i = 0;
-      for (; i + S::PF <= n_main; i += S::PF) {
+      if constexpr (WHOLE) {
+        for (int i = 0; i < n_main; i += S::PF) {
 #pragma unroll
-        for (int u = 0; u < S::PF; ++u) {
-          process(std::false_type{}, kb[u], vb[u], i + u);
-          // keep the refill of this slot after its use: hoisting the loads
-          // above the PV products would force a register copy of the tile
-          __builtin_amdgcn_sched_barrier(0);
-          issue(kb[u], vb[u], i + u + S::PF);
+          for (int u = 0; u < S::PF; ++u) {
+            if (i + u < n_main) {
+              process(std::false_type{}, kb[u], vb[u], i + u);
+              __builtin_amdgcn_sched_barrier(0);
+              issue(kb[u], vb[u], i + u + S::PF);
+            }
+          }
         }
-      }
+      } else {
+        int i = 0;
+        for (; i + S::PF <= n_main; i += S::PF) {
 #pragma unroll
-      for (int u = 0; u < S::PF - 1; ++u)
-        if (i + u < n_main) process(std::false_type{}, kb[u], vb[u], i + u);
+          for (int u = 0; u < S::PF; ++u) {
+            process(std::false_type{}, kb[u], vb[u], i + u);
+            // keep the refill of this slot after its use: hoisting the loads
+            // above the PV products would force a register copy of the tile
+            __builtin_amdgcn_sched_barrier(0);
+            issue(kb[u], vb[u], i + u + S::PF);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < S::PF - 1; ++u)
+          if (i + u < n_main) process(std::false_type{}, kb[u], vb[u], i + u);
+      }
       if (n_my > 0) {
         const int last = n_my - 1, slot = last % S::PF;
         const bool tail = blk0 + w + last * NW == nblk - 1;
