@@ -705,6 +705,17 @@ def bench_c4_mixed(args, fp8=False):
 
     ms_one_dec = _timed(one_launch_dec, max(1, args.steps // 4), max(1, args.warmup // 4))
     ms_one_pre = _timed(one_launch_pre, max(1, args.steps // 4), max(1, args.warmup // 4))
+    # the caller-side route rule (StepRunner, auto): time both routes on this
+    # step's size class, then report the route it keeps
+    runner = kvc.StepRunner(Hq, trials=3)
+    dec_part = dict(q=q_dec, k_new=k_dec, v_new=v_dec, block_table=bt_dec, context_lens=ctx_dec,
+                    max_context=max_dec)
+    pf_part = dict(q=q_pre, k=k_pre, v=v_pre, cu_chunk_lens=cu, prefix_lens=prefix,
+                   block_table=bt_pre, max_chunk=chunk)
+    for _ in range(8):
+        runner.run(cache, dec_part, pf_part)
+    torch.cuda.synchronize()
+    route_key = runner.size_class(nd, max_dec, npre * chunk)
     assert int(cache.err_flag.item()) == 0
     assert int(mws[:256].count_nonzero().item()) == 0
     # K and V per token and kv head: bf16 values, or fp8 codes plus two fp32 row scales
@@ -736,6 +747,10 @@ def bench_c4_mixed(args, fp8=False):
     res["one_launch_speedup"] = round(ms_step / ms_one, 3)
     res["one_launch_decode_only_ms"] = round(ms_one_dec, 4)
     res["one_launch_prefill_only_ms"] = round(ms_one_pre, 4)
+    res["step_route"] = {"chosen": runner.decisions.get(route_key),
+                         "separate_ms": [round(x, 4) for x in runner.samples[route_key]["separate"]],
+                         "one_launch_ms": [round(x, 4) for x in
+                                           runner.samples[route_key]["one_launch"]]}
     res["prefill_tflops"] = round(tf, 1)
     res["prefill_mfma_frac"] = round(tf / 2500.0, 4)
     print(json.dumps(res), flush=True)

@@ -351,7 +351,17 @@ size_t kvc_mixed_workspace_bytes(int32_t n_decode, int32_t decode_max_context, i
  * quantised (the codes and scales kvc_kv_append and the chunked-prefill calls
  * write), and q, k_new, v_new, the chunks' K/V and the outputs are bf16.
  * Returns KVC_ERR_WORKSPACE for a missing or short workspace and validates
- * like the two calls it replaces. */
+ * like the two calls it replaces.
+ * Route: the two separate calls are the default. On MI355X this one launch
+ * ties with them on a skewed 206-row decode batch with four 2,048-token
+ * chunks over bf16 (0.97-1.03x), and loses over fp8 (4%), on the steps of a
+ * 16-slot serving queue (20-27%) and on a uniform decode-only batch (8%):
+ * its decode waves keep fewer blocks in flight (its prefill items set its
+ * register budget).
+ * Callers that want the faster route per step without measuring it
+ * themselves can use the Python package's StepRunner, which takes the
+ * separate calls for single-kind steps and times both routes on the first
+ * steps of each size class of mixed steps. */
 int kvc_mixed_step_attention(const kvc_cache* cache, const kvc_mixed_batch* batch, int32_t Hq,
                              float softmax_scale, void* workspace, size_t workspace_bytes,
                              void* stream);

@@ -2,7 +2,8 @@
 AMD MI355X (gfx950): HIP kernels behind the C ABI in include/kvc.h, with this
 thin binding on top, and a host-side prefix-caching block manager
 (include/kvc_prefix.h), and an iteration-level scheduler that builds each
-step's batch descriptors (include/kvc_sched.h). Importing the package loads libkvc.so and raises if it is
+step's batch descriptors (include/kvc_sched.h), and a step runner that picks the faster launch
+route for a step of decode rows and prompt chunks (step.py). Importing the package loads libkvc.so and raises if it is
 missing; there is no CPU fallback.
 """
 from ._lib import (  # noqa: F401
@@ -37,3 +38,4 @@ from ._lib import (  # noqa: F401
     slot_mapping,
     stream_read,
 )
+from .step import ONE_LAUNCH, SEPARATE, StepRunner  # noqa: F401
