@@ -245,7 +245,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
   int32_t my_blk = -1;
   auto start_range = [&] {
     const int end = WHOLE ? min(blk0 + S::MAX_PART, blk_end) : blk_end;
-    n_my = (end - blk0 > w) ? (end - blk0 - w + NW - 1) / NW : 0;
+    // uniform across the wave (said so: the loop bounds and buffer
+    // descriptors that derive from it stay in scalar registers)
+    n_my = __builtin_amdgcn_readfirstlane((end - blk0 > w) ? (end - blk0 - w + NW - 1) / NW : 0);
     my_blk = lane < n_my ? bt_row[blk0 + w + lane * NW] : -1;
   };
   // the first range's block ids are loaded here, next to the query, so that
@@ -359,27 +361,21 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       }
     }
   };
-  float cur_sk[S::SPL], cur_sv[S::SPL];   // fp8: the row scales of the lane's QK tokens
-  u32x2 cur_v8[S::NI];                 // fp8: the block's V codes (the same units as vb)
-  // One block. TAIL marks the sequence's last block, the only one that can be
+  // One block, in three phases: score (its K tile to LDS and the scores of
+  // its tokens), weigh (the online-softmax update: running max and sum, the
+  // PV weights to LDS, the accumulators rescaled) and accumulate (the PV
+  // product). TAIL marks the sequence's last block, the only one that can be
   // partial or hold the appended token; every other block skips the masking
-  // and substitution code entirely.
-  auto process = [&](auto tail_tag, u32x4 (&kb)[S::NI], u32x4 (&vb)[S::NI], int i) {
+  // and substitution code entirely. fp8 passes the row scales of the lane's
+  // QK tokens (ks for the scores, vs for the weights) and its V codes.
+  auto score = [&](auto tail_tag, u32x4 (&kb)[S::NI], int i, const float (&ks)[S::SPL],
+                   float (&s)[S::SPL]) {
     constexpr bool TAIL = decltype(tail_tag)::value;
     const int lb = blk0 + w + i * NW;
-    if constexpr (TAIL) {
+    if constexpr (TAIL && !F8) {
 #pragma unroll
-      for (int j = 0; j < S::NI; ++j) {
-        const int tk = (j * 64 + lane) / S::NC;
-        if (!F8 && fuse && tk == t_new) {
-          kb[j] = k_new_c;
-          vb[j] = v_new_c;
-        }
-        if (lb * 16 + tk >= ctx) {                                 // unwritten rows may hold NaN
-          if constexpr (F8) cur_v8[j] = u32x2{0u, 0u};
-          else vb[j] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
+      for (int j = 0; j < S::NI; ++j)
+        if (fuse && (j * 64 + lane) / S::NC == t_new) kb[j] = k_new_c;
     }
     // K tile -> LDS, chunk c of token t at chunk slot c ^ (t % NC)
 #pragma unroll
@@ -388,8 +384,6 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       *reinterpret_cast<u32x4*>(kst + tk * S::RB + ((c ^ (tk % S::NC)) << 4)) = kb[j];
     }
     __builtin_amdgcn_wave_barrier();
-
-    float s[S::SPL];
 #pragma unroll
     for (int sl = 0; sl < S::SPL; ++sl) {
       const int t = tok(sl);
@@ -420,12 +414,16 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       const bool valid = active && (!TAIL || lb * 16 + t < ctx);
       if constexpr (F8) {
         // the key row's scale multiplies its dot product
-        s[sl] = valid ? dot * cur_sk[sl] * a.scale_log2 : -INFINITY;
+        s[sl] = valid ? dot * ks[sl] * a.scale_log2 : -INFINITY;
       } else {
         s[sl] = valid ? dot * a.scale_log2 : -INFINITY;
       }
     }
+  };
 
+  auto weigh = [&](auto tail_tag, int i, const float (&vs)[S::SPL], const float (&s)[S::SPL]) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const int lb = blk0 + w + i * NW;
     // online softmax over this block's tokens, per head (each token sits in
     // both lanes of its pair: harmless for the max, counted once in the sum)
     float mx = s[0];
@@ -453,7 +451,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       pw[sl] = p[sl];
       if constexpr (F8) {
         // rows past the context may hold NaN scales; their weight is 0
-        pw[sl] = (!TAIL || lb * 16 + tok(sl) < ctx) ? p[sl] * cur_sv[sl] : 0.f;
+        pw[sl] = (!TAIL || lb * 16 + tok(sl) < ctx) ? p[sl] * vs[sl] : 0.f;
       }
     }
     if (active && qh == 0) {
@@ -487,8 +485,27 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
 #pragma unroll
         for (int e = 0; e < S::CE; ++e) acc[hh][e] *= al[hh];
     }
+  };
 
-    // PV: lane owns chunk (lane % NC) of tokens j*TPI + lane / NC, j < NI
+  // PV: lane owns chunk (lane % NC) of tokens j*TPI + lane / NC, j < NI. vb
+  // holds bf16 / fp32 V chunks; v8 the fp8 V codes (8 per lane and load).
+  auto accumulate = [&](auto tail_tag, u32x4 (&vb)[S::NI], u32x2 (&v8)[S::NI], int i) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const int lb = blk0 + w + i * NW;
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int j = 0; j < S::NI; ++j) {
+        const int tk = (j * 64 + lane) / S::NC;
+        if (fuse && tk == t_new) {
+          if constexpr (F8) v8[j] = v_new_q;
+          else vb[j] = v_new_c;
+        }
+        if (lb * 16 + tk >= ctx) {                                 // unwritten rows may hold NaN
+          if constexpr (F8) v8[j] = u32x2{0u, 0u};
+          else vb[j] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
     if constexpr (S::DOT2_PV) {
       // tokens of loads (2m, 2m+1) form a pair; one v_dot2 per (head, dim) and pair
 #pragma unroll
@@ -502,7 +519,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
         if constexpr (F8) {
           // interleave the two tokens' code bytes, then convert pairs: each
           // E4M3 code is a bf16 value, so the pairs equal the bf16 path's
-          const u32x2 ca = cur_v8[2 * m], cb = cur_v8[2 * m + 1];
+          const u32x2 ca = v8[2 * m], cb = v8[2 * m + 1];
 #pragma unroll
           for (int w = 0; w < 2; ++w) {
             const uint32_t lo = __builtin_amdgcn_perm(cb[w], ca[w], 0x05010400u);   // a0 b0 a1 b1
@@ -542,38 +559,52 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     }
   };
 
-  // fp8: convert a ring slot's K codes to the bf16 tile the shared path reads
-  // and hand its V codes to the PV product as they are (with the new token's
-  // codes and scales in place for the tail block), then process it.
-  auto process8 = [&](auto tail_tag, u32x2 (&kr)[S::NI], u32x2 (&vr)[S::NI],
-                      const float (&sk)[S::SPL], const float (&sv)[S::SPL], int i) {
+  // bf16 / fp32: the three phases of one block in order.
+  auto process = [&](auto tail_tag, u32x4 (&kb)[S::NI], u32x4 (&vb)[S::NI], int i) {
+    float s[S::SPL];
+    const float none[S::SPL] = {};
+    u32x2 no8[S::NI];
+    score(tail_tag, kb, i, none, s);
+    weigh(tail_tag, i, none, s);
+    accumulate(tail_tag, vb, no8, i);
+  };
+
+  // fp8: a ring slot's K codes as the bf16 tile the shared path reads, and the
+  // row scales of the lane's QK tokens, with the new token's codes and scales
+  // in place for the tail block.
+  auto k_tile8 = [&](auto tail_tag, const u32x2 (&kr)[S::NI], u32x4 (&kb)[S::NI]) {
     constexpr bool TAIL = decltype(tail_tag)::value;
-    static_assert(S::DOT2_PV, "fp8 V codes go straight into the packed PV product");
-    u32x4 kb[S::NI], vb[S::NI] = {};   // vb unused: PV reads the codes in cur_v8
 #pragma unroll
     for (int j = 0; j < S::NI; ++j) {
-      u32x2 kx = kr[j], vx = vr[j];
+      u32x2 kx = kr[j];
       if constexpr (TAIL) {
-        if (fuse && (j * 64 + lane) / S::NC == t_new) {
-          kx = k_new_q;
-          vx = v_new_q;
-        }
+        if (fuse && (j * 64 + lane) / S::NC == t_new) kx = k_new_q;
       }
       kb[j] = e4m3x8_to_bf16x8(kx);
-      cur_v8[j] = vx;
     }
+  };
+  auto scales8 = [&](auto tail_tag, const float (&sc)[S::SPL], float new_s, float (&out)[S::SPL]) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
 #pragma unroll
     for (int sl = 0; sl < S::SPL; ++sl) {
-      cur_sk[sl] = sk[sl];
-      cur_sv[sl] = sv[sl];
+      out[sl] = sc[sl];
       if constexpr (TAIL) {
-        if (fuse && tok(sl) == t_new) {
-          cur_sk[sl] = k_new_s;
-          cur_sv[sl] = v_new_s;
-        }
+        if (fuse && tok(sl) == t_new) out[sl] = new_s;
       }
     }
-    process(tail_tag, kb, vb, i);
+  };
+  // fp8: the three phases of one block in order.
+  auto process8 = [&](auto tail_tag, u32x2 (&kr)[S::NI], u32x2 (&vr)[S::NI],
+                      const float (&sk)[S::SPL], const float (&sv)[S::SPL], int i) {
+    static_assert(S::DOT2_PV, "fp8 V codes go straight into the packed PV product");
+    u32x4 kb[S::NI], vb[S::NI];
+    float ks[S::SPL], vs[S::SPL], s[S::SPL];
+    k_tile8(tail_tag, kr, kb);
+    scales8(tail_tag, sk, k_new_s, ks);
+    scales8(tail_tag, sv, v_new_s, vs);
+    score(tail_tag, kb, i, ks, s);
+    weigh(tail_tag, i, vs, s);
+    accumulate(tail_tag, vb, vr, i);
   };
 
   // One range of blocks through the ring of PF blocks in flight.
@@ -586,15 +617,17 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     // the loop, the loop head would have to assume that the refills after it
     // were not made, and its waits for the oldest slot would drain the ring.
     // (The steps after the loop need no refill: every index they would load
-    // lies past the wave's blocks.) The mixed kernel's whole-sequence item
-    // keeps guarded turns: it has no registers to spare for the extra steps.
+    // lies past the wave's blocks.) The mixed kernel's whole-sequence item and
+    // G = 8 keep guarded turns: they have no registers to spare for the extra
+    // steps (at G = 8 the peeled steps would cost half the waves per SIMD:
+    // 5,767 against 4,511 GB/s for bf16 at 64 rows of 2k contexts).
     const int n_main = n_my > 0 ? n_my - 1 : 0;
     if constexpr (F8) {
       u32x2 kr[PF][S::NI], vr[PF][S::NI];
       float skr[PF][S::SPL], svr[PF][S::SPL];
 #pragma unroll
       for (int u = 0; u < PF; ++u) issue8(kr[u], vr[u], skr[u], svr[u], u);
-      if constexpr (WHOLE) {
+      if constexpr (WHOLE || G == 8) {
         for (int i = 0; i < n_main; i += PF) {
 #pragma unroll
           for (int u = 0; u < PF; ++u) {
@@ -640,7 +673,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       u32x4 kb[S::PF][S::NI], vb[S::PF][S::NI];
 #pragma unroll
       for (int u = 0; u < S::PF; ++u) issue(kb[u], vb[u], u);
-      if constexpr (WHOLE) {
+      if constexpr (WHOLE || G == 8) {
         for (int i = 0; i < n_main; i += S::PF) {
 #pragma unroll
           for (int u = 0; u < S::PF; ++u) {
