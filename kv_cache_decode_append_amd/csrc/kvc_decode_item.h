@@ -438,7 +438,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     for (int sl = 0; sl < S::SPL; ++sl) {
       p[sl] = __builtin_amdgcn_exp2f(s[sl] - m_safe);
       // bf16 PV multiplies by bf16 weights: round once here so that the
-      // normaliser l sums exactly the weights the numerator uses
+      // normaliser l sums exactly the weights the numerator uses. (fp8: the
+      // numerator's weight is this rounded p times the value row's scale,
+      // rounded to bf16 again below, so there l and the numerator differ by
+      // that second rounding, 2^-9 relative at most.)
       if constexpr (S::DOT2_PV) p[sl] = __uint_as_float(f32_to_bf16_bits(p[sl]) << 16);
       ps += (qh == 0) ? p[sl] : 0.f;
     }
