@@ -51,25 +51,21 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16). Over each group of 16
 // lanes, lane i addresses 4 consecutive 16-bit elements A_i; lane j receives
-// A_{4k + j/4}[j % 4] for k = 0..3. Issued as inline assembly: the compiler
-// makes the builtin wait for every buffer->LDS load in flight, which would
-// drain the tile prefetch. The caller waits for the result with
-// tr_read_ready before using it.
+// A_{4k + j/4}[j % 4] for k = 0..3. The compiler counts these reads with the
+// other LDS reads, so its waits for K and V fragments are exact. Without alias
+// information on the read it would also wait for every buffer->LDS load in
+// flight (draining the tile prefetch); the restrict parameter gives the
+// inlined read a scope of its own, as the plain K-fragment loads have. The
+// tile loads are ordered by the explicit waits and barriers that publish each
+// tile.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+__device__ __forceinline__ u32x2 tr_read_at(lds_s16x4* __restrict__ p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+}
 template <int OFF>
 __device__ __forceinline__ u32x2 tr_read_b64(uint32_t lds_addr) {
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "n"(OFF));
-  return r;
-}
-// Wait until at most `newer` pairs of transposing reads issued after (lo, hi)
-// are outstanding, i.e. until (lo, hi) have arrived; the register operands
-// order every use of the values after the wait.
-__device__ __forceinline__ void tr_read_ready(u32x2& lo, u32x2& hi, int newer) {
-  switch (newer) {
-    case 0: asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo), "+v"(hi)); break;
-    case 1: asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(lo), "+v"(hi)); break;
-    default: asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(lo), "+v"(hi)); break;
-  }
+  return tr_read_at(reinterpret_cast<lds_s16x4*>((uintptr_t)(lds_addr + OFF)));
 }
 
 template <typename T> struct PfMfma;
@@ -580,9 +576,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
   };
   // ---- V fragment (MFMA A operand of O^T += V^T . P^T) for key pair mp and
   // dim tile dt: keys 32mp + 4g + 0..3 and 32mp + 16 + 4g + 0..3 of dim
-  // 16dt + l16, in the key order of the S^T accumulators. Issued as two
-  // 8-byte halves; v_frag_use waits for them (row-major tiles; `newer` =
-  // fragments issued after this one) and joins them.
+  // 16dt + l16, in the key order of the S^T accumulators. Read as two
+  // 8-byte halves; v_frag_use joins them.
   struct VHalves { u32x2 lo, hi; };
   auto v_frag_issue = [&](const uint8_t* v_lds, int mp, int dt) -> VHalves {
     if constexpr (DMA) {
@@ -599,8 +594,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
       return {*reinterpret_cast<const u32x2*>(rowp), *reinterpret_cast<const u32x2*>(rowp + 16)};
     }
   };
-  auto v_frag_use = [&](VHalves& f, int newer) -> bf16x8_t {
-    if constexpr (DMA) tr_read_ready(f.lo, f.hi, newer);
+  auto v_frag_use = [&](const VHalves& f) -> bf16x8_t {
     return __builtin_bit_cast(bf16x8_t, u32x4{f.lo[0], f.lo[1], f.hi[0], f.hi[1]});
   };
   // ---- O^T += V^T . P^T for one tile; V fragments are read one step ahead
@@ -613,7 +607,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
         const int mp = st / S::DT, dt = st % S::DT;
         const bool more = st + 1 < 2 * S::DT;
         if (more) vf[(st + 1) & 1] = v_frag_issue(v_lds, (st + 1) / S::DT, (st + 1) % S::DT);
-        const bf16x8_t a = v_frag_use(vf[st & 1], more ? 1 : 0);
+        const bf16x8_t a = v_frag_use(vf[st & 1]);
 #pragma unroll
         for (int n = 0; n < kRowTiles; ++n)
           o[n][dt] = M::mma(a, __builtin_bit_cast(bf16x8_t, pt.v[mp][n]), o[n][dt]);
@@ -682,8 +676,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
       for (int st = 0; st < kSteps; ++st) {
         if (st + kAhead < kSteps) vf[(st + kAhead) % (kAhead + 1)] = frag(st + kAhead);
         const int mp = st / S::DT, dt = st % S::DT;
-        const int newer = kSteps - 1 - st < kAhead ? kSteps - 1 - st : kAhead;
-        const bf16x8_t va = v_frag_use(vf[st % (kAhead + 1)], newer);
+        const bf16x8_t va = v_frag_use(vf[st % (kAhead + 1)]);
   #pragma unroll
         for (int n = 0; n < kRowTiles; ++n)
           o[n][dt] = M::mma(va, __builtin_bit_cast(bf16x8_t, pt.v[mp][n]), o[n][dt]);
@@ -835,8 +828,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
         }
         if constexpr (PV) {
           if (st + 2 < kP) vf[(st + 2) % 3] = v_frag_issue(vl, (st + 2) / S::DT, (st + 2) % S::DT);
-          const int newer = kP - 1 - st < 2 ? kP - 1 - st : 2;
-          const bf16x8_t va = v_frag_use(vf[st % 3], newer);
+          const bf16x8_t va = v_frag_use(vf[st % 3]);
           const int mp = st / S::DT, dt = st % S::DT;
 #pragma unroll
           for (int nn = 0; nn < kRowTiles; ++nn)
