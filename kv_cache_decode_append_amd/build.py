@@ -31,6 +31,13 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 
 
+# Per-file device flags. The decode kernels' fp8 block step at head dim 128
+# keeps its MFMA accumulators in ordinary vector registers: the default
+# selection put them in the accumulation registers and copied them out and
+# back every block (136 extra instructions per two blocks).
+FILE_FLAGS = {"kvc_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
@@ -39,7 +46,7 @@ def compile_one(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
     cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
-        cmd[1:1] = ["-x", "hip", *DEVICE]
+        cmd[1:1] = ["-x", "hip", *DEVICE, *FILE_FLAGS.get(src, [])]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)

@@ -233,6 +233,32 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     for (int c = 0; c < S::NCQ; ++c) qv[c] = qp[qh * S::NCQ + c];
   }
 
+  // fp8 at head dim 128 (the standalone kernel): the block step runs on MFMA.
+  // Lane (mn = lane % 16, mg = lane / 16). QK: S[token][head] on
+  // v_mfma_f32_16x16x32_bf16, A = the K codes of token mn at dims 32mg ..
+  // 32mg+31 (k-step kk takes dims 32mg + 8kk .. +7, the same permutation of
+  // the head dim on both operands), B = the query of head mn at those dims;
+  // lane (mn, mg) ends with the scores of tokens 4mg .. 4mg+3 for head mn.
+  // PV: O[head][dim] on v_mfma_f32_16x16x16_bf16, A = the weights in exactly
+  // that layout (head mn, tokens 4mg .. 4mg+3), B = the V codes of the same
+  // four tokens at one dim, 8mn + dt for product dt, transposed in registers
+  // from the lane's own 8-byte loads (tokens 4mg .. 4mg+3, dims 8mn .. +7).
+  // No tile passes through LDS, and per block a lane issues about half the
+  // vector instructions of the dot-product form.
+  constexpr bool MF8 = F8 && D == 128 && !WHOLE;
+  const int mn = lane & 15, mg = lane >> 4;
+  bf16x8_t qb[4];
+  if constexpr (MF8) {
+    const int hq = kvh * G + (mn < G ? mn : 0);
+    const u32x4* qp = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const uint8_t*>(a.q) + ((size_t)b * hq_all + hq) * S::RB + 64 * mg);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const u32x4 qw = qp[kk];
+      qb[kk] = __builtin_bit_cast(bf16x8_t, mn < G ? qw : u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+
   const int32_t* bt_row = a.bt + (size_t)b * a.max_blocks;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kc);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vc);
@@ -315,7 +341,35 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     }
   };
 
+  // fp8 on MFMA: one ring slot (K codes of token mn, dims 32mg .. +31; V codes
+  // of tokens 4mg .. 4mg+3, dims 8mn .. +7; the K and V row scales of tokens
+  // 4mg .. 4mg+3)
+  struct Slot8M { u32x4 k[2]; u32x2 v[4]; f32x4 ks, vs; };
+  auto issue8m = [&](Slot8M& sl, int i) {
+    const int64_t tile = tile_of(i);
+    const size_t off = tile >= 0 ? (size_t)tile * TILE_MEM : 0;
+    const uint32_t bytes = tile >= 0 ? TILE_MEM : 0;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + off, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + off, bytes);
+    const __amdgpu_buffer_rsrc_t rks = make_rsrc(a.ks + (tile >= 0 ? tile * 16 : 0), tile >= 0 ? 64u : 0u);
+    const __amdgpu_buffer_rsrc_t rvs = make_rsrc(a.vs + (tile >= 0 ? tile * 16 : 0), tile >= 0 ? 64u : 0u);
+    sl.k[0] = buffer_load16_stream(rk, (uint32_t)(mn * D + 32 * mg));
+    sl.k[1] = buffer_load16_stream(rk, (uint32_t)(mn * D + 32 * mg + 16));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      sl.v[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                              rv, (uint32_t)((4 * mg + j) * D + 8 * mn), 0,
+                                              kCachePolicyNonTemporal));
+    sl.ks = __builtin_bit_cast(f32x4, buffer_load16_stream(rks, 16u * mg));
+    sl.vs = __builtin_bit_cast(f32x4, buffer_load16_stream(rvs, 16u * mg));
+  };
+
   float m_run = -INFINITY, l_run = 0.f;
+  f32x4 om[8];   // fp8 on MFMA: O[head 4mg + i][dim 8mn + dt] of product dt
+  if constexpr (MF8) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) om[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   float acc[G][S::CE];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
@@ -610,6 +664,115 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     accumulate(tail_tag, vb, vr, i);
   };
 
+  // fp8 on MFMA: one block. TAIL: the new row's codes and scales in place and
+  // rows past the context masked (their codes zeroed: unwritten rows may hold
+  // NaN codes, and a zero weight times NaN is NaN in the product).
+  auto process8m = [&](auto tail_tag, const Slot8M& sl, int i) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const int lb = blk0 + w + i * NW;
+    u32x4 kc0 = sl.k[0], kc1 = sl.k[1];
+    f32x4 ks = sl.ks, vs = sl.vs;
+    u32x2 v8[4] = {sl.v[0], sl.v[1], sl.v[2], sl.v[3]};
+    if constexpr (TAIL) {
+      if (fuse) {
+        // lane c holds the new row's codes of dims 8(c % 16) .. +7
+        u32x2 kn[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          kn[c] = u32x2{(uint32_t)__shfl((int)k_new_q.x, 4 * mg + c, 64),
+                        (uint32_t)__shfl((int)k_new_q.y, 4 * mg + c, 64)};
+        if (mn == t_new) {
+          kc0 = u32x4{kn[0].x, kn[0].y, kn[1].x, kn[1].y};
+          kc1 = u32x4{kn[2].x, kn[2].y, kn[3].x, kn[3].y};
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * mg + j == t_new) {
+            ks[j] = k_new_s;
+            vs[j] = v_new_s;
+            v8[j] = v_new_q;
+          }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (lb * 16 + 4 * mg + j >= ctx) v8[j] = u32x2{0u, 0u};
+    }
+    // QK^T on MFMA: codes to bf16 (exact), four k-steps of 32 dims
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const u32x4 kw = kk < 2 ? kc0 : kc1;
+      const uint32_t d0 = kw[(kk & 1) * 2], d1 = kw[(kk & 1) * 2 + 1];
+      const u32x4 kbf = u32x4{
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.f, false)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.f, true)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.f, false)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.f, true))};
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kbf), qb[kk], sc, 0, 0, 0);
+    }
+    // online softmax for head mn over tokens 4mg .. 4mg+3, the max across the
+    // four lane groups; the row sum stays per lane until the end
+    float s[4], mx = -INFINITY;
+    bool valid[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      valid[j] = mn < G && (!TAIL || lb * 16 + 4 * mg + j < ctx);
+      // the key row's scale multiplies its dot product
+      s[j] = valid[j] ? sc[j] * ks[j] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    mx = rows_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_safe);
+    float ps = 0.f;
+    uint32_t pb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // the weight rounded to bf16 once (the sum adds it); the PV weight is it
+      // times the value row's scale, rounded again
+      const float p = __uint_as_float(f32_to_bf16_bits(__builtin_amdgcn_exp2f(s[j] - m_safe)) << 16);
+      ps += p;
+      pb[j] = valid[j] ? f32_to_bf16_bits(p * vs[j]) : 0u;
+    }
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    const u32x2 pa = u32x2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+    // rescale the accumulators when a running max moved: row i of a lane's
+    // products is head 4mg + i, whose factor lane 4mg + i holds
+    if (__builtin_expect(__ballot(mn < G && alpha != 1.f) != 0, 0)) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float al = __shfl(alpha, 4 * mg + j, 64);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) om[dt][j] *= al;
+      }
+    }
+    // PV on MFMA: each 4-byte half of the lane's token rows transposed to
+    // (4 tokens) x (one dim) code words, then converted to bf16
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const uint32_t t0 = v8[0][h2], t1 = v8[1][h2], t2 = v8[2][h2], t3 = v8[3][h2];
+      const uint32_t lo01 = __builtin_amdgcn_perm(t1, t0, 0x05010400u);   // t0b0 t1b0 t0b1 t1b1
+      const uint32_t hi01 = __builtin_amdgcn_perm(t1, t0, 0x07030602u);   // t0b2 t1b2 t0b3 t1b3
+      const uint32_t lo23 = __builtin_amdgcn_perm(t3, t2, 0x05010400u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(t3, t2, 0x07030602u);
+      const uint32_t dd[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),    // dim 4h2 + 0
+                              __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),    // dim 4h2 + 1
+                              __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),    // dim 4h2 + 2
+                              __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};   // dim 4h2 + 3
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const u32x2 vb = u32x2{
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dd[e], 1.f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dd[e], 1.f, true))};
+        om[4 * h2 + e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            __builtin_bit_cast(s16x4, pa), __builtin_bit_cast(s16x4, vb), om[4 * h2 + e], 0, 0, 0);
+      }
+    }
+  };
+
   // One range of blocks through the ring of PF blocks in flight.
   auto run_range = [&] {
     // Ring of PF blocks in flight; a slot is refilled right after it is used.
@@ -625,7 +788,53 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     // steps (at G = 8 the peeled steps would cost half the waves per SIMD:
     // 5,767 against 4,511 GB/s for bf16 at 64 rows of 2k contexts).
     const int n_main = n_my > 0 ? n_my - 1 : 0;
-    if constexpr (F8) {
+    if constexpr (MF8) {
+      Slot8M slot[PF];
+#pragma unroll
+      for (int u = 0; u < PF; ++u) issue8m(slot[u], u);
+      if constexpr (G == 8) {
+        for (int i = 0; i < n_main; i += PF) {
+#pragma unroll
+          for (int u = 0; u < PF; ++u) {
+            if (i + u < n_main) {
+              process8m(std::false_type{}, slot[u], i + u);
+              __builtin_amdgcn_sched_barrier(0);
+              issue8m(slot[u], i + u + PF);
+            }
+          }
+        }
+      } else {
+        int i = 0;
+        for (; i + PF <= n_main; i += PF) {
+#pragma unroll
+          for (int u = 0; u < PF; ++u) {
+            process8m(std::false_type{}, slot[u], i + u);
+            __builtin_amdgcn_sched_barrier(0);
+            issue8m(slot[u], i + u + PF);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < PF - 1; ++u)
+          if (i + u < n_main) process8m(std::false_type{}, slot[u], i + u);
+      }
+      if (n_my > 0) {
+        const int last = n_my - 1, slot_last = last % PF;
+        const bool tail = blk0 + w + last * NW == nblk - 1;
+        if (tail && fuse) {
+          quantise_new();
+          has_tail = true;
+        }
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          if (u == slot_last) {
+            if (tail)
+              process8m(std::true_type{}, slot[u], last);
+            else
+              process8m(std::false_type{}, slot[u], last);
+          }
+        }
+      }
+    } else if constexpr (F8) {
       u32x2 kr[PF][S::NI], vr[PF][S::NI];
       float skr[PF][S::SPL], svr[PF][S::SPL];
 #pragma unroll
@@ -746,8 +955,21 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
 
   // merge the four wave states
   __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);   // [NW][TPI][G][D]
-  {
+  constexpr int RSUB = MF8 ? 1 : S::TPI;          // partial sums per wave, head and dim
+  float* red = reinterpret_cast<float*>(smem);   // [NW][RSUB][G][D]
+  if constexpr (MF8) {
+    l_run = rows_sum(l_run);                     // the four lane groups' partial row sums
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int hh = 4 * mg + j;
+      if (hh < G) {
+        float* dst = red + (w * G + hh) * D + 8 * mn;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{om[0][j], om[1][j], om[2][j], om[3][j]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{om[4][j], om[5][j], om[6][j], om[7][j]};
+      }
+    }
+    if (mg == 0 && mn < G) ml[w * G + mn] = make_float2(m_run, l_run);
+  } else {
     const int sub = lane / S::NC, cc = lane % S::NC;
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
@@ -771,7 +993,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       const float f = (st.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.x - M);
       float sum = 0.f;
 #pragma unroll
-      for (int sub = 0; sub < S::TPI; ++sub) sum += red[((ww * S::TPI + sub) * G + hh) * D + d];
+      for (int sub = 0; sub < RSUB; ++sub) sum += red[((ww * RSUB + sub) * G + hh) * D + d];
       L += st.y * f;
       A += sum * f;
     }
