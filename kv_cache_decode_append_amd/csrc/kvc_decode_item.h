@@ -235,9 +235,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
 
   // fp8 at head dim 128 (the standalone kernel): the block step runs on MFMA.
   // Lane (mn = lane % 16, mg = lane / 16). QK: S[token][head] on
-  // v_mfma_f32_16x16x32_bf16, A = the K codes of token mn at dims 32mg ..
-  // 32mg+31 (k-step kk takes dims 32mg + 8kk .. +7, the same permutation of
-  // the head dim on both operands), B = the query of head mn at those dims;
+  // v_mfma_f32_16x16x32_bf16, A = the K codes of token mn, B = the query of
+  // head mn, at the same eight dims per k-step (any permutation of the head
+  // dim taken on both operands gives the same dot product); the four lanes of
+  // a token read 64 contiguous bytes of its row per load, dims 16mg .. +15
+  // and 64 + 16mg .. +15 (k-steps 0, 1 and 2, 3);
   // lane (mn, mg) ends with the scores of tokens 4mg .. 4mg+3 for head mn.
   // PV: O[head][dim] on v_mfma_f32_16x16x16_bf16, A = the weights in exactly
   // that layout (head mn, tokens 4mg .. 4mg+3), B = the V codes of the same
@@ -246,15 +248,22 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
   // No tile passes through LDS, and per block a lane issues about half the
   // vector instructions of the dot-product form.
   constexpr bool MF8 = F8 && D == 128 && !WHOLE;
+  // bf16 at head dim 128: the same products, k-step kk on dims 32kk + 8mg
+  // .. +7 of token mn (again 64 contiguous bytes per token and load), and V
+  // transposed in 16-bit halves
+  constexpr bool MB16 = std::is_same_v<T, bf16_tag> && D == 128 && !WHOLE;
+  constexpr bool MFP = MF8 || MB16;
   const int mn = lane & 15, mg = lane >> 4;
   bf16x8_t qb[4];
-  if constexpr (MF8) {
+  if constexpr (MFP) {
     const int hq = kvh * G + (mn < G ? mn : 0);
-    const u32x4* qp = reinterpret_cast<const u32x4*>(
-        reinterpret_cast<const uint8_t*>(a.q) + ((size_t)b * hq_all + hq) * S::RB + 64 * mg);
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + ((size_t)b * hq_all + hq) * S::RB;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const u32x4 qw = qp[kk];
+      // k-step kk, lane group mg: dims 32kk + 8mg .. +7 (bf16); fp8 takes
+      // dims 16mg + 8kk .. +7 for kk < 2 and 64 + 16mg + 8(kk - 2) .. +7
+      const int qb_off = MB16 ? 64 * kk + 16 * mg : (kk < 2 ? 32 * mg + 16 * kk : 128 + 32 * mg + 16 * (kk - 2));
+      const u32x4 qw = *reinterpret_cast<const u32x4*>(qrow + qb_off);
       qb[kk] = __builtin_bit_cast(bf16x8_t, mn < G ? qw : u32x4{0u, 0u, 0u, 0u});
     }
   }
@@ -353,8 +362,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + off, bytes);
     const __amdgpu_buffer_rsrc_t rks = make_rsrc(a.ks + (tile >= 0 ? tile * 16 : 0), tile >= 0 ? 64u : 0u);
     const __amdgpu_buffer_rsrc_t rvs = make_rsrc(a.vs + (tile >= 0 ? tile * 16 : 0), tile >= 0 ? 64u : 0u);
-    sl.k[0] = buffer_load16_stream(rk, (uint32_t)(mn * D + 32 * mg));
-    sl.k[1] = buffer_load16_stream(rk, (uint32_t)(mn * D + 32 * mg + 16));
+    // the four lanes of a token read 64 contiguous bytes per load: dims
+    // 16mg .. +15 and 64 + 16mg .. +15
+    sl.k[0] = buffer_load16_stream(rk, (uint32_t)(mn * D + 16 * mg));
+    sl.k[1] = buffer_load16_stream(rk, (uint32_t)(mn * D + 64 + 16 * mg));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       sl.v[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
@@ -365,8 +376,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
   };
 
   float m_run = -INFINITY, l_run = 0.f;
-  f32x4 om[8];   // fp8 on MFMA: O[head 4mg + i][dim 8mn + dt] of product dt
-  if constexpr (MF8) {
+  f32x4 om[8];   // MFMA step: O[head 4mg + i][dim 8mn + dt] of product dt
+  if constexpr (MFP) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) om[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -675,12 +686,15 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     u32x2 v8[4] = {sl.v[0], sl.v[1], sl.v[2], sl.v[3]};
     if constexpr (TAIL) {
       if (fuse) {
-        // lane c holds the new row's codes of dims 8(c % 16) .. +7
+        // lane c holds the new row's codes of dims 8(c % 16) .. +7; this
+        // lane's are chunks 2mg, 2mg + 1, 8 + 2mg, 9 + 2mg
         u32x2 kn[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          kn[c] = u32x2{(uint32_t)__shfl((int)k_new_q.x, 4 * mg + c, 64),
-                        (uint32_t)__shfl((int)k_new_q.y, 4 * mg + c, 64)};
+        for (int c = 0; c < 4; ++c) {
+          const int src = (c < 2 ? 0 : 8) + 2 * mg + (c & 1);
+          kn[c] = u32x2{(uint32_t)__shfl((int)k_new_q.x, src, 64),
+                        (uint32_t)__shfl((int)k_new_q.y, src, 64)};
+        }
         if (mn == t_new) {
           kc0 = u32x4{kn[0].x, kn[0].y, kn[1].x, kn[1].y};
           kc1 = u32x4{kn[2].x, kn[2].y, kn[3].x, kn[3].y};
@@ -750,7 +764,6 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     }
     // PV on MFMA: each 4-byte half of the lane's token rows transposed to
     // (4 tokens) x (one dim) code words, then converted to bf16
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const uint32_t t0 = v8[0][h2], t1 = v8[1][h2], t2 = v8[2][h2], t3 = v8[3][h2];
@@ -768,7 +781,107 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dd[e], 1.f, false)),
             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dd[e], 1.f, true))};
         om[4 * h2 + e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            __builtin_bit_cast(s16x4, pa), __builtin_bit_cast(s16x4, vb), om[4 * h2 + e], 0, 0, 0);
+            __builtin_bit_cast(s16x4_t, pa), __builtin_bit_cast(s16x4_t, vb), om[4 * h2 + e], 0, 0, 0);
+      }
+    }
+  };
+
+  // bf16 on MFMA: one ring slot (K chunks of token mn, dims 32c + 8mg .. +7
+  // for k-step c; V chunks of tokens 4mg .. 4mg+3, dims 8mn .. +7) and one
+  // block
+  auto issue16m = [&](u32x4 (&kk4)[4], u32x4 (&vv4)[4], int i) {
+    size_t off = 0;
+    uint32_t bytes = 0;
+    if (i < n_my) {
+      const int blk = __builtin_amdgcn_readlane(my_blk, i);
+      if ((unsigned)blk < (unsigned)a.num_blocks) {
+        off = ((size_t)blk * a.hkv + kvh) * S::TILE;
+        bytes = S::TILE;
+      } else if (lane == 0) {
+        flag_error(a.err, KVC_DEVERR_BLOCK_ID);
+      }
+    }
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + off, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + off, bytes);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kk4[c] = buffer_load16_stream(rk, (uint32_t)(mn * S::RB + 64 * c + 16 * mg));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vv4[j] = buffer_load16_stream(rv, (uint32_t)((4 * mg + j) * S::RB + 16 * mn));
+  };
+  auto process16m = [&](auto tail_tag, const u32x4 (&kk4)[4], const u32x4 (&vv4)[4], int i) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const int lb = blk0 + w + i * NW;
+    u32x4 kc[4] = {kk4[0], kk4[1], kk4[2], kk4[3]};
+    u32x4 vc[4] = {vv4[0], vv4[1], vv4[2], vv4[3]};
+    if constexpr (TAIL) {
+      if (fuse) {
+        // lane c holds the new row's dims 8(c % 16) .. +7; k-step c takes
+        // chunk 4c + mg
+        u32x4 kn[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kn[c][e] = (uint32_t)__shfl((int)k_new_c[e], 4 * c + mg, 64);
+        if (mn == t_new) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) kc[c] = kn[c];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * mg + j == t_new) vc[j] = v_new_c;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (lb * 16 + 4 * mg + j >= ctx) vc[j] = u32x4{0u, 0u, 0u, 0u};   // unwritten rows may hold NaN
+    }
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kc[kk]), qb[kk], sc, 0, 0, 0);
+    float s[4], mx = -INFINITY;
+    bool valid[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      valid[j] = mn < G && (!TAIL || lb * 16 + 4 * mg + j < ctx);
+      s[j] = valid[j] ? sc[j] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    mx = rows_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_safe);
+    float ps = 0.f;
+    uint32_t pb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // bf16 PV multiplies by bf16 weights: round once, and the sum adds the
+      // rounded weights
+      const uint32_t bits = f32_to_bf16_bits(__builtin_amdgcn_exp2f(s[j] - m_safe));
+      ps += __uint_as_float(bits << 16);
+      pb[j] = valid[j] ? bits : 0u;
+    }
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    const u32x2 pa = u32x2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+    if (__builtin_expect(__ballot(mn < G && alpha != 1.f) != 0, 0)) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float al = __shfl(alpha, 4 * mg + j, 64);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) om[dt][j] *= al;
+      }
+    }
+    // PV: word e of each token chunk holds dims 8mn + 2e, 2e + 1; pair the
+    // four tokens' halves per dim
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
+        const u32x2 vb = u32x2{__builtin_amdgcn_perm(vc[1][e], vc[0][e], sel),
+                               __builtin_amdgcn_perm(vc[3][e], vc[2][e], sel)};
+        om[2 * e + hi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            __builtin_bit_cast(s16x4_t, pa), __builtin_bit_cast(s16x4_t, vb), om[2 * e + hi], 0, 0, 0);
       }
     }
   };
@@ -881,6 +994,48 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
           }
         }
       }
+    } else if constexpr (MB16) {
+      u32x4 k4[S::PF][4], v4[S::PF][4];
+#pragma unroll
+      for (int u = 0; u < S::PF; ++u) issue16m(k4[u], v4[u], u);
+      if constexpr (G == 8) {
+        for (int i = 0; i < n_main; i += S::PF) {
+#pragma unroll
+          for (int u = 0; u < S::PF; ++u) {
+            if (i + u < n_main) {
+              process16m(std::false_type{}, k4[u], v4[u], i + u);
+              __builtin_amdgcn_sched_barrier(0);
+              issue16m(k4[u], v4[u], i + u + S::PF);
+            }
+          }
+        }
+      } else {
+        int i = 0;
+        for (; i + S::PF <= n_main; i += S::PF) {
+#pragma unroll
+          for (int u = 0; u < S::PF; ++u) {
+            process16m(std::false_type{}, k4[u], v4[u], i + u);
+            __builtin_amdgcn_sched_barrier(0);
+            issue16m(k4[u], v4[u], i + u + S::PF);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < S::PF - 1; ++u)
+          if (i + u < n_main) process16m(std::false_type{}, k4[u], v4[u], i + u);
+      }
+      if (n_my > 0) {
+        const int last = n_my - 1, slot_last = last % S::PF;
+        const bool tail = blk0 + w + last * NW == nblk - 1;
+#pragma unroll
+        for (int u = 0; u < S::PF; ++u) {
+          if (u == slot_last) {
+            if (tail)
+              process16m(std::true_type{}, k4[u], v4[u], last);
+            else
+              process16m(std::false_type{}, k4[u], v4[u], last);
+          }
+        }
+      }
     } else {
       u32x4 kb[S::PF][S::NI], vb[S::PF][S::NI];
 #pragma unroll
@@ -955,9 +1110,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
 
   // merge the four wave states
   __syncthreads();
-  constexpr int RSUB = MF8 ? 1 : S::TPI;          // partial sums per wave, head and dim
+  constexpr int RSUB = MFP ? 1 : S::TPI;          // partial sums per wave, head and dim
   float* red = reinterpret_cast<float*>(smem);   // [NW][RSUB][G][D]
-  if constexpr (MF8) {
+  if constexpr (MFP) {
     l_run = rows_sum(l_run);                     // the four lane groups' partial row sums
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

@@ -12,6 +12,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));   // 4 x 16-bit MFMA operand
 
 // Storage tag for bfloat16 elements (raw 16-bit patterns).
 struct bf16_tag {};

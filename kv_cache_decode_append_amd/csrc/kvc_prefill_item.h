@@ -58,7 +58,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 // inlined read a scope of its own, as the plain K-fragment loads have. The
 // tile loads are ordered by the explicit waits and barriers that publish each
 // tile.
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 __device__ __forceinline__ u32x2 tr_read_at(lds_s16x4* __restrict__ p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
