@@ -407,13 +407,14 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
   // fp8: the new row's codes (this lane's 8 values) and scales, quantised as
   // kv_append does (the NC lanes of each group hold the whole row). The wave
   // that processes the last block makes them there, just before it, so that
-  // nothing of the new row is held in registers through the loop.
+  // nothing of the new row is held in registers through the loop; the MFMA
+  // step (few registers) loads the row before its loop and quantises it
+  // there, so that no load latency sits between its last two blocks.
   u32x2 k_new_q = u32x2{0u, 0u}, v_new_q = u32x2{0u, 0u};
   float k_new_s = 0.f, v_new_s = 0.f;
   bool has_tail = false;   // fp8: this wave processed the sequence's last block
-  auto quantise_new = [&] {
+  auto quantise_loaded = [&] {
     if constexpr (F8) {
-      load_new();
       const float ka = group_max<S::NC>(bf16x8_amax(k_new_c));
       const float va = group_max<S::NC>(bf16x8_amax(v_new_c));
       if (ka >= kZeroRowAmax) {
@@ -425,6 +426,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
         v_new_s = va / kE4M3Max;
       }
     }
+  };
+  auto quantise_new = [&] {
+    load_new();
+    quantise_loaded();
   };
   // One block, in three phases: score (its K tile to LDS and the scores of
   // its tokens), weigh (the online-softmax update: running max and sum, the
@@ -902,6 +907,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     // 5,767 against 4,511 GB/s for bf16 at 64 rows of 2k contexts).
     const int n_main = n_my > 0 ? n_my - 1 : 0;
     if constexpr (MF8) {
+      const bool tail_here = fuse && n_my > 0 && blk0 + w + (n_my - 1) * NW == nblk - 1;
+      if (tail_here) load_new();
       Slot8M slot[PF];
 #pragma unroll
       for (int u = 0; u < PF; ++u) issue8m(slot[u], u);
@@ -933,8 +940,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       if (n_my > 0) {
         const int last = n_my - 1, slot_last = last % PF;
         const bool tail = blk0 + w + last * NW == nblk - 1;
-        if (tail && fuse) {
-          quantise_new();
+        if (tail_here) {
+          quantise_loaded();
           has_tail = true;
         }
 #pragma unroll
