@@ -233,7 +233,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     for (int c = 0; c < S::NCQ; ++c) qv[c] = qp[qh * S::NCQ + c];
   }
 
-  // fp8 at head dim 128 (the standalone kernel): the block step runs on MFMA.
+  // fp8 at head dim 128: the block step runs on MFMA.
   // Lane (mn = lane % 16, mg = lane / 16). QK: S[token][head] on
   // v_mfma_f32_16x16x32_bf16, A = the K codes of token mn, B = the query of
   // head mn, at the same eight dims per k-step (any permutation of the head
@@ -247,10 +247,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
   // from the lane's own 8-byte loads (tokens 4mg .. 4mg+3, dims 8mn .. +7).
   // No tile passes through LDS, and per block a lane issues about half the
   // vector instructions of the dot-product form.
-  constexpr bool MF8 = F8 && D == 128 && !WHOLE;
-  // bf16 at head dim 128: the same products, k-step kk on dims 32kk + 8mg
-  // .. +7 of token mn (again 64 contiguous bytes per token and load), and V
-  // transposed in 16-bit halves
+  constexpr bool MF8 = F8 && D == 128;
+  // bf16 at head dim 128 (the standalone kernel; the mixed kernel's
+  // whole-sequence item keeps the dot-product step, which is as fast there):
+  // the same products, k-step kk on dims 32kk + 8mg .. +7 of token mn (again
+  // 64 contiguous bytes per token and load), and V transposed in 16-bit halves
   constexpr bool MB16 = std::is_same_v<T, bf16_tag> && D == 128 && !WHOLE;
   constexpr bool MFP = MF8 || MB16;
   const int mn = lane & 15, mg = lane >> 4;
@@ -912,7 +913,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       Slot8M slot[PF];
 #pragma unroll
       for (int u = 0; u < PF; ++u) issue8m(slot[u], u);
-      if constexpr (G == 8) {
+      if constexpr (WHOLE || G == 8) {
         for (int i = 0; i < n_main; i += PF) {
 #pragma unroll
           for (int u = 0; u < PF; ++u) {
@@ -1005,7 +1006,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       u32x4 k4[S::PF][4], v4[S::PF][4];
 #pragma unroll
       for (int u = 0; u < S::PF; ++u) issue16m(k4[u], v4[u], u);
-      if constexpr (G == 8) {
+      if constexpr (WHOLE || G == 8) {
         for (int i = 0; i < n_main; i += S::PF) {
 #pragma unroll
           for (int u = 0; u < S::PF; ++u) {
