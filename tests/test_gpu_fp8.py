@@ -267,11 +267,12 @@ MIXED_CASES = [
     (16, 8, 128, [16, 33, 1000], [37], [300]),
     (8, 2, 64, [1, 65, 2500], [0, 250], [130, 17]),
     (32, 8, 128, _LONG, [2000], [300]),          # 640 decode items: rows ordered longest first
+    (8, 8, 128, [1, 40, 1500, 4100], [0], [33]),  # G = 1 on the MFMA step's 16 head columns
 ]
 
 
 @pytest.mark.parametrize("Hq,Hkv,D,dec_ctx,pf_prefix,pf_chunk", MIXED_CASES,
-                         ids=["4-heads-mix", "g2", "d64", "80-rows"])
+                         ids=["4-heads-mix", "g2", "d64", "80-rows", "g1"])
 def test_mixed_step_over_fp8_cache(kvc, Hq, Hkv, D, dec_ctx, pf_prefix, pf_chunk):
     """The one-launch mixed step over an fp8 cache against the same step as
     separate calls (fused append + decode, then chunk write + prefill): the
