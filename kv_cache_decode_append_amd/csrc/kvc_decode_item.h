@@ -27,6 +27,11 @@
 //     is read once per step), in a register ring of 2-3 blocks per wave. A
 //     buffer descriptor of zero bytes turns the prefetch past the wave's last
 //     block into a no-op with no memory traffic.
+//   * At head dim 128 (bf16 in the decode kernel, fp8 in both kernels) the
+//     block step runs on MFMA: QK and PV are two matrix products in one lane
+//     layout, straight from the loaded registers (see the MFMA step below). The
+//     other head dims, fp32 and the mixed kernel's bf16 item take the
+//     dot-product step:
 //   * QK: K goes to a per-wave LDS tile with an XOR swizzle of its 16-byte
 //     chunks (conflict-free row reads); lane (h, t) computes the full dot product
 //     of query head h with token t's key (bf16: v_dot2_f32_bf16, fp32: FMA), so
