@@ -736,33 +736,38 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kbf), qb[kk], sc, 0, 0, 0);
     }
     // online softmax for head mn over tokens 4mg .. 4mg+3, the max across the
-    // four lane groups; the row sum stays per lane until the end
+    // four lane groups; the row sum stays per lane until the end. Only the
+    // tail block masks: every other block's rows are written, and lanes of
+    // heads past G (zero query, so zero scores) hold finite values that are
+    // never stored.
     float s[4], mx = -INFINITY;
-    bool valid[4];
+    float vsm[4] = {vs[0], vs[1], vs[2], vs[3]};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      valid[j] = mn < G && (!TAIL || lb * 16 + 4 * mg + j < ctx);
       // the key row's scale multiplies its dot product
-      s[j] = valid[j] ? sc[j] * ks[j] * a.scale_log2 : -INFINITY;
+      s[j] = sc[j] * ks[j] * a.scale_log2;
+      if constexpr (TAIL) {
+        // rows past the context may hold any bits, their scales too
+        const bool valid = mn < G && lb * 16 + 4 * mg + j < ctx;
+        s[j] = valid ? s[j] : -INFINITY;
+        vsm[j] = valid ? vsm[j] : 0.f;
+      }
       mx = fmaxf(mx, s[j]);
     }
     mx = rows_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_safe);
-    float ps = 0.f;
-    uint32_t pb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // the weight rounded to bf16 once (the sum adds it); the PV weight is it
-      // times the value row's scale, rounded again
-      const float p = __uint_as_float(f32_to_bf16_bits(__builtin_amdgcn_exp2f(s[j] - m_safe)) << 16);
-      ps += p;
-      pb[j] = valid[j] ? f32_to_bf16_bits(p * vs[j]) : 0u;
-    }
+    // the weights rounded to bf16 once, two per conversion (the sum adds
+    // them); the PV weights are them times the value rows' scales, rounded
+    // again, packed as the products take them
+    const uint32_t e01 = pack_bf16x2(__builtin_amdgcn_exp2f(s[0] - m_safe), __builtin_amdgcn_exp2f(s[1] - m_safe));
+    const uint32_t e23 = pack_bf16x2(__builtin_amdgcn_exp2f(s[2] - m_safe), __builtin_amdgcn_exp2f(s[3] - m_safe));
+    const float p[4] = {bf16_lo(e01), bf16_hi(e01), bf16_lo(e23), bf16_hi(e23)};
+    const float ps = ((p[0] + p[1]) + p[2]) + p[3];
     l_run = l_run * alpha + ps;
     m_run = m_new;
-    const u32x2 pa = u32x2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+    const u32x2 pa = u32x2{pack_bf16x2(p[0] * vsm[0], p[1] * vsm[1]), pack_bf16x2(p[2] * vsm[2], p[3] * vsm[3])};
     // rescale the accumulators when a running max moved: row i of a lane's
     // products is head 4mg + i, whose factor lane 4mg + i holds
     if (__builtin_expect(__ballot(mn < G && alpha != 1.f) != 0, 0)) {
@@ -849,31 +854,27 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kc[kk]), qb[kk], sc, 0, 0, 0);
+    // only the tail block masks (see the fp8 step); its rows past the context
+    // have zero values, so a zero weight is all they need
     float s[4], mx = -INFINITY;
-    bool valid[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      valid[j] = mn < G && (!TAIL || lb * 16 + 4 * mg + j < ctx);
-      s[j] = valid[j] ? sc[j] * a.scale_log2 : -INFINITY;
+      s[j] = sc[j] * a.scale_log2;
+      if constexpr (TAIL) s[j] = (mn < G && lb * 16 + 4 * mg + j < ctx) ? s[j] : -INFINITY;
       mx = fmaxf(mx, s[j]);
     }
     mx = rows_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_safe);
-    float ps = 0.f;
-    uint32_t pb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // bf16 PV multiplies by bf16 weights: round once, and the sum adds the
-      // rounded weights
-      const uint32_t bits = f32_to_bf16_bits(__builtin_amdgcn_exp2f(s[j] - m_safe));
-      ps += __uint_as_float(bits << 16);
-      pb[j] = valid[j] ? bits : 0u;
-    }
+    // bf16 PV multiplies by bf16 weights: round once, two per conversion, and
+    // the sum adds the rounded weights; the pairs are the products' operand
+    const u32x2 pa = u32x2{
+        pack_bf16x2(__builtin_amdgcn_exp2f(s[0] - m_safe), __builtin_amdgcn_exp2f(s[1] - m_safe)),
+        pack_bf16x2(__builtin_amdgcn_exp2f(s[2] - m_safe), __builtin_amdgcn_exp2f(s[3] - m_safe))};
+    const float ps = ((bf16_lo(pa[0]) + bf16_hi(pa[0])) + bf16_lo(pa[1])) + bf16_hi(pa[1]);
     l_run = l_run * alpha + ps;
     m_run = m_new;
-    const u32x2 pa = u32x2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
     if (__builtin_expect(__ballot(mn < G && alpha != 1.f) != 0, 0)) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
