@@ -251,6 +251,35 @@ def test_decode_at_140k_context_many_partitions(kvc):
     _check_case(kvc, case, what="split-K 140k", fused=True)
 
 
+def _random_batches(seed, n):
+    """Seeded batch shapes: group size, kv heads, contexts (at block, partition
+    and ragged boundaries), plain or fused."""
+    rng = np.random.default_rng(seed)
+    lens = [1, 2, 15, 16, 17, 31, 33, 255, 257, 1000, 2049, 4100]
+    out = []
+    for _ in range(n):
+        g, hkv, b = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2, 3, 8])), int(rng.integers(1, 9))
+        out.append((g, hkv, [int(x) for x in rng.choice(lens, size=b)], bool(rng.integers(0, 2))))
+    return out
+
+
+SWEEP = _random_batches(73, 12)
+
+
+@pytest.mark.parametrize("g,hkv,ctx,fused", SWEEP, ids=[f"s{i}" for i in range(len(SWEEP))])
+def test_random_batches_bf16_d128(kvc, g, hkv, ctx, fused):
+    """Seeded random batches through the bf16 block step at head dim 128 (the
+    MFMA step of the decode kernel): group sizes 1-8, 1-8 kv heads, 1-8 rows
+    whose contexts cross block and partition boundaries, plain and fused;
+    against the oracle, and the pool bit for bit."""
+    i = SWEEP.index((g, hkv, ctx, fused))
+    say(f"random batch {i}: G={g} Hkv={hkv} ctx {ctx} fused {fused}")
+    w = W.small_workload(f"sweep-{i}", 900 + i, B=len(ctx), Hq=g * hkv, Hkv=hkv, D=128, dtype="bf16",
+                         sigma=0.5)
+    case = DecodeCase(w, ctx, sum(W.blocks_for(c) for c in ctx) + 8, seed_extra=i)
+    _check_case(kvc, case, what=f"random batch {i}", fused=fused)
+
+
 def test_split_k_agrees_with_one_partition(kvc):
     """The same 3,000-token sequence decoded as row 0 of a 64-row batch (one
     partition: the batch already fills 512 workgroups) and alone (12

@@ -139,6 +139,35 @@ def test_decode_over_fp8_cache_matches_oracle(kvc, Hq, Hkv, D, ctx):
     say(f"  max abs err {worst:.2e}")
 
 
+def _random_fp8_batches(seed, n):
+    rng = np.random.default_rng(seed)
+    lens = [1, 2, 15, 16, 17, 33, 257, 1000, 2049, 4100]
+    return [(int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2, 8])),
+             [int(x) for x in rng.choice(lens, size=int(rng.integers(1, 7)))]) for _ in range(n)]
+
+
+FP8_SWEEP = _random_fp8_batches(78, 8)
+
+
+@pytest.mark.parametrize("g,hkv,ctx", FP8_SWEEP, ids=[f"s{i}" for i in range(len(FP8_SWEEP))])
+def test_random_batches_fp8_d128(kvc, g, hkv, ctx):
+    """Seeded random batches through the fp8 block step at head dim 128 (the
+    MFMA step): group sizes 1-8, 1-8 kv heads, contexts across block and
+    partition boundaries; against the oracle over the dequantised cache."""
+    i = FP8_SWEEP.index((g, hkv, ctx))
+    case = Fp8Case(950 + i, g * hkv, hkv, 128, ctx, seed_extra=i)
+    say(f"fp8 random batch {i}: G={g} Hkv={hkv} ctx {ctx}")
+    cache, btd = case.fill(kvc)
+    out = kvc.paged_decode_attention(cache, _dev(case.qb), btd,
+                                     torch.from_numpy(case.ctx.astype(np.int32)).cuda(),
+                                     int(case.ctx.max()))
+    torch.cuda.synchronize()
+    assert int(cache.err_flag.item()) == 0
+    got = out.float().cpu().numpy()
+    for b in range(len(ctx)):
+        assert_close(got[b], case.oracle(b), "bf16", f"fp8 random batch {i} row {b}")
+
+
 def test_fused_append_decode_equals_append_then_decode(kvc):
     case = Fp8Case(560, 32, 8, 128, [1, 2, 16, 17, 31, 400, 3000, 2048], seed_extra=3)
     say("fp8 fused append + decode vs append then decode")
