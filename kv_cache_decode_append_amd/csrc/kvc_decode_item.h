@@ -351,8 +351,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
 #pragma unroll
     for (int sl = 0; sl < S::SPL; ++sl) {
       const uint32_t soff = (uint32_t)tok(sl) * 4u;
-      sk[sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, soff, 0, kCachePolicyNonTemporal));
-      sv[sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, soff, 0, kCachePolicyNonTemporal));
+      sk[sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, soff, 0, 0));   // default policy,
+      sv[sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, soff, 0, 0));   // as in the MFMA step
     }
   };
 
@@ -377,8 +377,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
       sl.v[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                                               rv, (uint32_t)((4 * mg + j) * D + 8 * mn), 0,
                                               kCachePolicyNonTemporal));
-    sl.ks = __builtin_bit_cast(f32x4, buffer_load16_stream(rks, 16u * mg));
-    sl.vs = __builtin_bit_cast(f32x4, buffer_load16_stream(rvs, 16u * mg));
+    // the scales with the default cache policy: the kv heads' scale rows of
+    // one block sit side by side, and their workgroups (one per XCD) read
+    // them close together, so the shared cache serves most of them
+    sl.ks = __builtin_bit_cast(f32x4, buffer_load16(rks, 16u * mg));
+    sl.vs = __builtin_bit_cast(f32x4, buffer_load16(rvs, 16u * mg));
   };
 
   float m_run = -INFINITY, l_run = 0.f;
