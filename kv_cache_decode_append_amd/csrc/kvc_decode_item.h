@@ -372,15 +372,18 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     // 16mg .. +15 and 64 + 16mg .. +15
     sl.k[0] = buffer_load16_stream(rk, (uint32_t)(mn * D + 16 * mg));
     sl.k[1] = buffer_load16_stream(rk, (uint32_t)(mn * D + 64 + 16 * mg));
+    // each row scale right after the codes it scales, in the order the block
+    // step consumes them: the in-order load counter then lets the softmax
+    // start before the V codes land. The scales take the default cache
+    // policy: the kv heads' scale rows of one block sit side by side, and
+    // their workgroups (one per XCD) read them close together, so the shared
+    // cache serves most of them.
+    sl.ks = __builtin_bit_cast(f32x4, buffer_load16(rks, 16u * mg));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       sl.v[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                                               rv, (uint32_t)((4 * mg + j) * D + 8 * mn), 0,
                                               kCachePolicyNonTemporal));
-    // the scales with the default cache policy: the kv heads' scale rows of
-    // one block sit side by side, and their workgroups (one per XCD) read
-    // them close together, so the shared cache serves most of them
-    sl.ks = __builtin_bit_cast(f32x4, buffer_load16(rks, 16u * mg));
     sl.vs = __builtin_bit_cast(f32x4, buffer_load16(rvs, 16u * mg));
   };
 
