@@ -201,6 +201,18 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hq_all = a.hkv * G;
 
+  // The block ids of this wave's first range, read before the context length
+  // is known, so that the two reads overlap instead of following each other:
+  // the range starts at part * part_blocks whatever the length, every entry
+  // of the table row is safe to read, and the entries past the sequence's
+  // blocks are dropped once the length is known. (The mixed kernel's
+  // whole-sequence item reads its ranges as it reaches them.)
+  int32_t first_ids = -1;
+  if constexpr (!WHOLE) {
+    const int idx = part * a.part_blocks + w + lane * NW;
+    if (idx < a.max_blocks && lane * NW + w < a.part_blocks) first_ids = a.bt[(size_t)b * a.max_blocks + idx];
+  }
+
   bool ctx_ok;
   const int ctx = effective_ctx(a, b, part == 0 && kvh == 0 && tid == 0, &ctx_ok);
   const int nblk = (ctx + 15) >> 4;
@@ -289,7 +301,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int b,
     // uniform across the wave (said so: the loop bounds and buffer
     // descriptors that derive from it stay in scalar registers)
     n_my = __builtin_amdgcn_readfirstlane((end - blk0 > w) ? (end - blk0 - w + NW - 1) / NW : 0);
-    my_blk = lane < n_my ? bt_row[blk0 + w + lane * NW] : -1;
+    my_blk = lane < n_my ? (WHOLE ? bt_row[blk0 + w + lane * NW] : first_ids) : -1;
   };
   // the first range's block ids are loaded here, next to the query, so that
   // the loads of the new row below are not behind them in the load counter
