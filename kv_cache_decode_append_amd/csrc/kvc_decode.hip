@@ -11,6 +11,7 @@ namespace kvc {
 
 constexpr int kWaves = 4;
 constexpr int kMaxPartBlocks = kWaves * 64;   // one block id per lane of each wave
+constexpr int64_t kMinWorkBlocks = 32;        // blocks a partition should hold when split
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a) {
@@ -136,6 +137,14 @@ int decode_part_blocks(int B, int hkv, int nblk_max, int cus) {
   const int64_t max_parts = (nblk_max + kMinPartBlocks - 1) / kMinPartBlocks;
   if (n_part > max_parts) n_part = max_parts;
   if (n_part < 1) n_part = 1;
+  // Fewer, longer partitions where a partition would hold few blocks (about 8
+  // per wave or fewer): each one's fixed costs (the ring fill, the wave merge,
+  // its partial and its share of the merge pass) then outweigh the fuller
+  // chip. Halving keeps a power-of-two grid at whole multiples of the CU
+  // count (one GPU's share under kv-head x8, 64 rows of ~2k tokens: 4
+  // partitions, 4,095 against 3,787 GB/s with 8; 5 or 6 partitions, which
+  // give some CUs two workgroups and others one, measured 3,477 and 3,566).
+  while (n_part > 1 && (int64_t)nblk_max < kMinWorkBlocks * n_part) n_part = (n_part + 1) / 2;
   int64_t pb = (nblk_max + n_part - 1) / n_part;
   pb = (pb + 3) / 4 * 4;
   if (pb < kMinPartBlocks) pb = kMinPartBlocks;
