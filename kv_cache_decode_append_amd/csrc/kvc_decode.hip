@@ -32,39 +32,65 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
 // are read in one round and the maximum and the normaliser come from wave
 // reductions. Each lane then adds the partials of its D/64 output dims in
 // partition order, eight partitions' loads in flight at a time, each weight
-// read from the lane that holds its partition.
+// read from the lane that holds its partition. The first 64 (m, l) pairs and
+// the first eight partitions' partials are read together with the context
+// length, before the count of partitions in use is known: the reads stay in
+// this row's n_part slots, and what lies past the last used partition (stale
+// workspace) is replaced by the neutral value before any arithmetic.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int32_t hq_all) {
   const int row = blockIdx.x;                 // b * Hq + hq
   const int b = row / hq_all;
+  const int lane = threadIdx.x;
+  const float2* ml = a.ws_ml + (size_t)row * a.n_part;
+  const float* po = a.ws_o + (size_t)row * a.n_part * D;
+  constexpr int E = D >= 64 ? D / 64 : 1;     // output dims per lane
+  const bool has = D >= 64 || lane < D;
+  const int n_pre = min(8, a.n_part);
+  float2 ml0 = make_float2(-INFINITY, 0.f);
+  if (lane < a.n_part) ml0 = ml[lane];
+  float x0[8][E];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int e = 0; e < E; ++e) x0[u][e] = (has && u < n_pre) ? po[(size_t)u * D + lane * E + e] : 0.f;
   const int ctx = effective_ctx(a, b, false);
   const int nblk = (ctx + 15) >> 4;
   const int n_used = nblk > 0 ? (nblk + a.part_blocks - 1) / a.part_blocks : 1;
   if (n_used <= 1) return;
-  const int lane = threadIdx.x;
-  const float2* ml = a.ws_ml + (size_t)row * a.n_part;
-  const float* po = a.ws_o + (size_t)row * a.n_part * D;
   float m_lane = -INFINITY;
-  for (int i = lane; i < n_used; i += 64) m_lane = fmaxf(m_lane, ml[i].x);
+  if (lane < n_used) m_lane = fmaxf(m_lane, ml0.x);
+  for (int i = lane + 64; i < n_used; i += 64) m_lane = fmaxf(m_lane, ml[i].x);
   const float M = rows_max(group_max<16>(m_lane));
   float l_lane = 0.f;
-  for (int i = lane; i < n_used; i += 64) l_lane += ml[i].y * __builtin_amdgcn_exp2f(ml[i].x - M);
+  if (lane < n_used) l_lane += ml0.y * __builtin_amdgcn_exp2f(ml0.x - M);
+  for (int i = lane + 64; i < n_used; i += 64) l_lane += ml[i].y * __builtin_amdgcn_exp2f(ml[i].x - M);
   const float inv = 1.f / rows_sum(group_sum<16>(l_lane));
-  constexpr int E = D >= 64 ? D / 64 : 1;     // output dims per lane
-  const bool has = D >= 64 || lane < D;
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   for (int c = 0; c < n_used; c += 64) {      // 64 partitions per round
-    const float w = c + lane < n_used ? __builtin_amdgcn_exp2f(ml[c + lane].x - M) : 0.f;
+    float w = 0.f;
+    if (c == 0) {
+      if (lane < n_used) w = __builtin_amdgcn_exp2f(ml0.x - M);
+    } else if (c + lane < n_used) {
+      w = __builtin_amdgcn_exp2f(ml[c + lane].x - M);
+    }
     const int n = min(64, n_used - c);
     for (int j0 = 0; j0 < n; j0 += 8) {
       float x[8][E];
+      if (c == 0 && j0 == 0) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-          x[u][e] = (has && j0 + u < n) ? po[(size_t)(c + j0 + u) * D + lane * E + e] : 0.f;
+          for (int e = 0; e < E; ++e) x[u][e] = u < n ? x0[u][e] : 0.f;
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            x[u][e] = (has && j0 + u < n) ? po[(size_t)(c + j0 + u) * D + lane * E + e] : 0.f;
+      }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float wu = readlane_f(w, j0 + u);   // 0 past the last partition
