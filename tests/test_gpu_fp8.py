@@ -225,15 +225,28 @@ def test_quantisation_error_within_its_bound(kvc):
     say(f"fp8 vs bf16 cache: worst error / max|out| = {worst_rel:.3e}")
 
 
+def _random_fp8_prefill(seed, n):
+    """Seeded head-dim-128 prefill shapes over an fp8 cache: group size, kv
+    heads, prefixes and chunks on and beside the block and key-tile edges."""
+    rng = np.random.default_rng(seed)
+    pre, chk = [0, 1, 16, 63, 65, 500, 1700], [1, 16, 17, 64, 65, 200]
+    out = []
+    for _ in range(n):
+        g, hkv, b = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2, 3])), int(rng.integers(1, 4))
+        out.append((g * hkv, hkv, 128, [int(x) for x in rng.choice(pre, size=b)],
+                    [int(x) for x in rng.choice(chk, size=b)]))
+    return out
+
+
 PF_CASES = [
     (32, 8, 128, [0, 37, 300, 2000], [1, 17, 300, 200]),
     (8, 2, 64, [5, 100], [70, 9]),
     (16, 2, 64, [0, 3000], [130, 64]),
-]
+] + _random_fp8_prefill(83, 4)
 
 
 @pytest.mark.parametrize("Hq,Hkv,D,prefix,chunk", PF_CASES,
-                         ids=[f"{c[0]}/{c[1]}/{c[2]}" for c in PF_CASES])
+                         ids=[f"{c[0]}/{c[1]}/{c[2]}-{i}" for i, c in enumerate(PF_CASES)])
 @pytest.mark.parametrize("split", [False, True])
 def test_chunked_prefill_over_fp8_cache(kvc, Hq, Hkv, D, prefix, chunk, split):
     """Prefill chunks written into an fp8 cache (quantised as kv_append does)

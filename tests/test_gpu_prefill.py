@@ -149,6 +149,39 @@ def test_split_keys_short_chunks_over_long_prefixes(kvc, dtype, d, g):
     _check(kvc, case, f"split {dtype} D={d} G={g}", max_context_len=max_ctx)
 
 
+def _random_prefill_batches(seed, n):
+    """Seeded batch shapes for the MFMA prefill at head dim 128: group size, kv
+    heads, prefix and chunk lengths on and beside the 16-token block and the
+    64-key tile boundaries (prefixes long enough for the key-range split to
+    cut), through the plain or the split entry point."""
+    rng = np.random.default_rng(seed)
+    pre = [0, 1, 15, 16, 63, 64, 65, 255, 700, 1500, 2600]
+    chk = [1, 2, 16, 17, 63, 64, 65, 129, 256, 300]
+    out = []
+    for _ in range(n):
+        g, hkv, b = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2, 3])), int(rng.integers(1, 5))
+        out.append((g, hkv, [int(x) for x in rng.choice(pre, size=b)],
+                    [int(x) for x in rng.choice(chk, size=b)], bool(rng.integers(0, 2))))
+    return out
+
+
+PF_SWEEP = _random_prefill_batches(91, 10)
+
+
+@pytest.mark.parametrize("g,hkv,prefix,chunk,split", PF_SWEEP, ids=[f"p{i}" for i in range(len(PF_SWEEP))])
+def test_random_batches_bf16_d128(kvc, g, hkv, prefix, chunk, split):
+    """Seeded random batches through the bf16 prefill at head dim 128 (the
+    two-group MFMA pipeline): every row against the oracle, the pool bit for
+    bit."""
+    i = PF_SWEEP.index((g, hkv, prefix, chunk, split))
+    total = [p + c for p, c in zip(prefix, chunk)]
+    say(f"random prefill {i}: G={g} Hkv={hkv} prefix {prefix} chunk {chunk} split {split}")
+    w = W.small_workload(f"pf-sweep-{i}", 3100 + i, B=len(prefix), Hq=g * hkv, Hkv=hkv, D=128,
+                         dtype="bf16", sigma=0.5)
+    case = PrefillCase(w, prefix, chunk, sum(W.blocks_for(t) for t in total) + 4, seed_extra=i)
+    _check(kvc, case, f"random prefill {i}", max_context_len=max(total) if split else None)
+
+
 def test_split_entry_without_split_is_the_same_kernel(kvc):
     """C5-sized work needs no split: the split entry point gives the plain call's bits."""
     say("prefill split entry, no split needed: bitwise equal to the plain call")
