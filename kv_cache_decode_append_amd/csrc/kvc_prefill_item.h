@@ -205,9 +205,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
   using M = PfMfma<CT>;
   using Frag = typename M::Frag;
   constexpr int RB_MEM = F8 ? D : S::RB;              // bytes of one cached row
-  // bf16 caches of 64 / 128 dims: K and V tiles go from the pool straight
-  // into LDS (buffer->LDS loads), three tiles deep
-  constexpr bool DMA = S::DMA_OK && !F8;
+  // bf16 and fp8 caches of 64 / 128 dims run the two-group pipeline over
+  // row-major swizzled tiles; bf16 tiles go from the pool straight into LDS
+  // (buffer->LDS loads), fp8 tiles through registers, converted on the way
+  constexpr bool TWO = S::DMA_OK;
+  constexpr bool DMA = TWO && !F8;
   int32_t* bt_lds = reinterpret_cast<int32_t*>(smem + S::TILES);
   const int qt = work % a.n_qt;
   const int sp = (work / a.n_qt) % a.n_split;
@@ -352,7 +354,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
   auto v_swz = [](int key) { return 2 * (key % (S::NC / 2)); };
   // V fragment read offsets inside a tile, per dim tile (see v_frag_issue)
   int v_off[S::DT];
-  if constexpr (DMA) {
+  if constexpr (TWO) {
     const int v_row = 4 * g + (l16 >> 2);
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
@@ -579,7 +581,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
   // 8-byte halves; v_frag_use joins them.
   struct VHalves { u32x2 lo, hi; };
   auto v_frag_issue = [&](const uint8_t* v_lds, int mp, int dt) -> VHalves {
-    if constexpr (DMA) {
+    if constexpr (TWO) {
       // row-major tile: each transposing read gathers 4 keys x 16 dims over a
       // 16-lane group; lane i of the group addresses key 4g + i/4, dims
       // 16dt + 4(i%4) .. +3 (chunk swizzle of that key's row applied)
@@ -721,7 +723,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
 #pragma unroll
     for (int n = 0; n < kRowTiles; ++n) asm volatile("" : "+v"(l_run[n]));
   };
-  if constexpr (DMA) {
+  if constexpr (TWO) {
     // Two groups of four waves with one wave of each on every SIMD (waves w
     // and w + 4 share a SIMD). Each group alternates a matrix half-step
     // (QK^T of tile k and PV of tile k - 1: 64 MFMAs, fragments from LDS)
@@ -771,6 +773,42 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
                                                  voff, 0, 0, 0);
       }
     };
+    // fp8: the same tiles staged through registers. A wave reads its block of
+    // a tile (codes and row scales; the chunk order the swizzle puts in each
+    // lane's 16-byte slot) in one vector half-step and writes it, converted
+    // to bf16, lane after lane in its next one. An absent block reads inside
+    // the pool's first block; it and keys past the sequence are written as
+    // zeros.
+    u32x2 st_codes[BPB];
+    float st_scale[BPB];
+    bool st_ok[BPB];
+    auto fetch8 = [&](int k, const uint8_t* pool, const float* scales) {
+      const int kt = t_begin + k;
+      const int r = __builtin_amdgcn_readfirstlane(block_row(kt * 4 + wi, 4 * k < S::BT_CACHE));
+      const uint8_t* base = pool + (r >= 0 ? (int64_t)r * (16 * RB_MEM) : 0);
+      const float* sc = scales + (r >= 0 ? (int64_t)r * 16 : 0);
+      const int key0 = kt * kKeyTile + wi * 16;
+#pragma unroll
+      for (int j = 0; j < BPB; ++j) {
+        const int kb = j * kKeysPerDma + lane / S::NC, key = wi * 16 + kb;
+        const int swz = grp == 1 ? key % S::NC : v_swz(key);
+        st_codes[j] = *reinterpret_cast<const u32x2*>(base + kb * RB_MEM + (((lane % S::NC) ^ swz) << 3));
+        st_scale[j] = sc[kb];
+        st_ok[j] = r >= 0 && key0 + kb < kv_len;
+      }
+    };
+    auto put8 = [&](uint8_t* lds) {
+#pragma unroll
+      for (int j = 0; j < BPB; ++j)
+        *reinterpret_cast<u32x4*>(lds + (wi * BPB + j) * 1024 + lane * 16) =
+            zero_unless(st_ok[j], dequant(st_codes[j], st_scale[j]));
+    };
+    // fp8 tiles ahead of their use: at vector(k) group 1 writes K(k + NB - 1)
+    // (into the buffer K(k - 1) left at half-step 2k - 1; read from 2k + 2NB - 2)
+    // and group 0 V(k + NB - 3) (V(k - 3) was last read at 2k - 3; read from
+    // 2k + 4), then each reads the next tile of its kind into registers
+    const int put_lead = grp == 1 ? NB - 1 : NB - 3;
+
     // end of a half-step: this wave's LDS reads are done and, if `wait`, at
     // most `newer` of its staging batches are still in flight; then the barrier
     static_assert(NB >= 3 && NB <= 4, "newer batches: 0 .. 2");
@@ -845,14 +883,30 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
       // one call site, its pool, buffer and tile chosen by selects (two call
       // sites, one per group, were merged by the compiler into a block that
       // left the K pool's base unset on group 1's path)
-      const int ks = grp == 1 ? k + NB : k + NB - 2;
-      if (ks < n_t) stage(ks, grp == 1 ? kbase : vbase, grp == 1 ? kbuf(ks) : vbuf(ks));
-      half_step_end(true, newer_batches(k));
+      if constexpr (F8) {
+        const int kp = k + put_lead;
+        if (kp < n_t) put8(grp == 1 ? kbuf(kp) : vbuf(kp));
+        if (kp + 1 < n_t) fetch8(kp + 1, grp == 1 ? kbase : vbase, grp == 1 ? a.ks : a.vs);
+        half_step_end(false, 0);
+      } else {
+        const int ks = grp == 1 ? k + NB : k + NB - 2;
+        if (ks < n_t) stage(ks, grp == 1 ? kbase : vbase, grp == 1 ? kbuf(ks) : vbuf(ks));
+        half_step_end(true, newer_batches(k));
+      }
     };
 
     // prologue: K(0 .. NB-1) by group 1, V(0 .. NB-3) by group 0; K(0) and
     // K(1) must have landed before the first matrix half-steps
-    {
+    if constexpr (F8) {
+      // fp8: K(0 .. NB-2) by group 1, V(0 .. NB-4) by group 0 written now,
+      // the next tile of each kind read into registers
+      for (int k = 0; k < min(put_lead, n_t); ++k) {
+        fetch8(k, grp == 1 ? kbase : vbase, grp == 1 ? a.ks : a.vs);
+        put8(grp == 1 ? kbuf(k) : vbuf(k));
+      }
+      if (put_lead < n_t) fetch8(put_lead, grp == 1 ? kbase : vbase, grp == 1 ? a.ks : a.vs);
+      half_step_end(false, 0);
+    } else {
       const int n_pro = min(grp == 1 ? NB : NB - 2, n_t);
       for (int k = 0; k < n_pro; ++k) stage(k, grp == 1 ? kbase : vbase, grp == 1 ? kbuf(k) : vbuf(k));
       half_step_end(grp == 1, newer_batches(-1));      // group 1: K(2 .. NB-1) may stay in flight
