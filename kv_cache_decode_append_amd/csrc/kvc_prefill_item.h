@@ -111,9 +111,10 @@ struct PfShape {
   static constexpr int VCH = BF16 ? 2 : 1;          // chunks per V unit
   static constexpr int K_LDS = kKeyTile * RB;
   static constexpr int V_LDS = BF16 ? D * VT_STRIDE * 2 : kKeyTile * RB;
-  // bf16 tiles of 64 and 128 dims are staged by buffer->LDS loads into NBUF
-  // K and NBUF V buffers, both row-major with a chunk swizzle; the others go
-  // through registers into two K and two (transposed) V buffers
+  // tiles of 64 and 128 bf16 dims (bf16 or fp8 caches) go into NBUF K and
+  // NBUF V buffers, both row-major with a chunk swizzle (bf16 by buffer->LDS
+  // loads, fp8 through registers); the others go through registers into two K
+  // and two (transposed) V buffers
   static constexpr bool DMA_OK = BF16 && NC >= 8;
   static constexpr int NBUF = 4;
   static constexpr int BPB = 16 * RB / 1024;        // 1 KB staging loads per 16-token block
@@ -361,8 +362,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
       v_off[dt] = v_row * S::RB + (((2 * dt + ((l16 & 3) >> 1)) ^ v_swz(v_row)) << 4) + (l16 & 1) * 8;
   }
 
-  // Register staging of K and V tiles. K runs two tiles ahead of V (QK^T of
-  // tile k+1 is computed before PV of tile k), so each is loaded on its own.
+  // Register staging of K and V tiles for the lockstep pipeline (fp32 caches
+  // and 32 dims). K runs two tiles ahead of V (QK^T of tile k+1 is computed
+  // before PV of tile k), so each is loaded on its own.
   constexpr bool kAllK = S::K_UNITS % kPfThreads == 0;   // every thread has every K unit
   constexpr bool kAllV = S::V_UNITS % kPfThreads == 0;
   u32x4 kr[S::KPT], vr[S::VPT][S::VCH];
