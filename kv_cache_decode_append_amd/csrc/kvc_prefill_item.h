@@ -332,12 +332,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
   // 16 bytes (chunk c) of key `key` of tile kt. An absent key loads from the
   // pool's first row (always valid) and is zeroed when stored to LDS, so no
   // wait for the load lands here.
-  struct Row16 { int64_t off; bool ok; int64_t row; };
+  struct Row16 { int64_t off; bool ok; };
   auto locate = [&](int kt, int key, bool cached) -> Row16 {
     const int r = block_row(kt * 4 + (key >> 4), cached);
     const bool ok = r >= 0 && kt * kKeyTile + key < kv_len;
-    return {ok ? (int64_t)r * (16 * RB_MEM) + (key & 15) * RB_MEM : 0, ok,
-            ok ? (int64_t)r * 16 + (key & 15) : 0};
+    return {ok ? (int64_t)r * (16 * RB_MEM) + (key & 15) * RB_MEM : 0, ok};
   };
   auto zero_unless = [](bool ok, const u32x4& v) { return ok ? v : u32x4{0u, 0u, 0u, 0u}; };
 
@@ -369,9 +368,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
   constexpr bool kAllV = S::V_UNITS % kPfThreads == 0;
   u32x4 kr[S::KPT], vr[S::VPT][S::VCH];
   bool kok[S::KPT], vok[S::VPT][S::VCH];
-  // fp8: the codes of the same (key, 8 values) units and their rows' scales
-  u32x2 kr8[S::KPT], vr8[S::VPT][S::VCH];
-  float ksc[S::KPT], vsc[S::VPT][S::VCH];
+  static_assert(!F8 || TWO, "fp8 tiles are staged by the two-group pipeline only");
+  // fp8 codes (8 of them) times their row's scale, rounded to bf16
   auto dequant = [](const u32x2& w, float sc) {
     const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
     const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
@@ -394,12 +392,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
           block_row(kt * 4 + __builtin_amdgcn_readfirstlane(key >> 4), cached));
       const uint8_t* base = kbase + (r >= 0 ? (int64_t)r * (16 * RB_MEM) : 0);
       kok[j] = has && r >= 0 && kt * kKeyTile + key < kv_len;
-      if constexpr (F8) {
-        kr8[j] = *reinterpret_cast<const u32x2*>(base + (key & 15) * RB_MEM + (ci % S::NC) * 8);
-        ksc[j] = a.ks[(r >= 0 ? (int64_t)r * 16 : 0) + (key & 15)];
-      } else {
-        kr[j] = *reinterpret_cast<const u32x4*>(base + (key & 15) * S::RB + (ci % S::NC) * 16);
-      }
+      kr[j] = *reinterpret_cast<const u32x4*>(base + (key & 15) * S::RB + (ci % S::NC) * 16);
     }
   };
   auto load_v = [&](int kt) {
@@ -416,12 +409,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
         const int c = S::BF16 ? u / (kKeyTile / 2) : u % S::NC;
         const Row16 rw = locate(kt, key, cached);
         vok[j][x] = has && rw.ok;
-        if constexpr (F8) {
-          vr8[j][x] = *reinterpret_cast<const u32x2*>(vbase + rw.off + c * 8);
-          vsc[j][x] = a.vs[rw.row];
-        } else {
-          vr[j][x] = *reinterpret_cast<const u32x4*>(vbase + rw.off + c * 16);
-        }
+        vr[j][x] = *reinterpret_cast<const u32x4*>(vbase + rw.off + c * 16);
       }
     }
   };
@@ -431,7 +419,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
       const int ci = tid + j * kPfThreads;
       if (kAllK || ci < S::K_UNITS) {
         const int key = ci / S::NC, c = ci % S::NC;
-        if constexpr (F8) kr[j] = dequant(kr8[j], ksc[j]);
         *reinterpret_cast<u32x4*>(k_lds + key * S::RB + ((c ^ (key % S::NC)) << 4)) =
             zero_unless(kok[j], kr[j]);
       }
@@ -442,10 +429,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
     for (int j = 0; j < S::VPT; ++j) {
       const int u = tid + j * kPfThreads;
       if (!kAllV && u >= S::V_UNITS) continue;
-      if constexpr (F8) {
-#pragma unroll
-        for (int x = 0; x < S::VCH; ++x) vr[j][x] = dequant(vr8[j][x], vsc[j][x]);
-      }
       const u32x4 v0 = zero_unless(vok[j][0], vr[j][0]);
       const u32x4 v1 = zero_unless(vok[j][S::VCH - 1], vr[j][S::VCH - 1]);
       if constexpr (S::BF16) {
