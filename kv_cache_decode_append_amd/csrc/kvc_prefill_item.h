@@ -296,10 +296,15 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
 
   f32x4 o[kRowTiles][S::DT];
   float m_run[kRowTiles], l_run[kRowTiles];
+  // two-group pipeline: each row's sum of weights comes from the matrix cores,
+  // as the product of an all-ones V^T fragment with the same bf16 weights PV
+  // uses, rescaled like the output; every element holds the lane's row sum
+  f32x4 osum[kRowTiles];
 #pragma unroll
   for (int n = 0; n < kRowTiles; ++n) {
     m_run[n] = -INFINITY;
     l_run[n] = 0.f;
+    osum[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt) o[n][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -541,15 +546,18 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
           if constexpr (!S::BF16) rs += p[m][i];
         }
       if constexpr (S::BF16) {
-        // the row sum adds the bf16 weights the PV product uses
+        // the row sum adds the bf16 weights the PV product uses (in the
+        // two-group pipeline the matrix cores add them)
 #pragma unroll
         for (int mp = 0; mp < 2; ++mp) {
           pt.v[mp][n] = u32x4{pack_bf16x2(p[2 * mp][0], p[2 * mp][1]),
                               pack_bf16x2(p[2 * mp][2], p[2 * mp][3]),
                               pack_bf16x2(p[2 * mp + 1][0], p[2 * mp + 1][1]),
                               pack_bf16x2(p[2 * mp + 1][2], p[2 * mp + 1][3])};
+          if constexpr (!TWO) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) rs = dot2_bf16(pt.v[mp][n][q], kBf16OnePair, rs);
+            for (int q = 0; q < 4; ++q) rs = dot2_bf16(pt.v[mp][n][q], kBf16OnePair, rs);
+          }
         }
       } else {
 #pragma unroll
@@ -557,7 +565,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
 #pragma unroll
           for (int i = 0; i < 4; ++i) pt.v[m][n][i] = p[m][i];
       }
-      l_run[n] = fmaf(l_run[n], alpha[n], rs);
+      if constexpr (!TWO) l_run[n] = fmaf(l_run[n], alpha[n], rs);
     }
   };
   // ---- V fragment (MFMA A operand of O^T += V^T . P^T) for key pair mp and
@@ -681,6 +689,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
       if (__builtin_expect(__any(alpha[n] != 1.f), 0)) {   // wave-uniform: skip when no max moved
 #pragma unroll
         for (int dt = 0; dt < S::DT; ++dt) o[n][dt] *= alpha[n];
+        if constexpr (TWO) osum[n] *= alpha[n];
       }
   };
 
@@ -855,6 +864,13 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
 #pragma unroll
           for (int nn = 0; nn < kRowTiles; ++nn)
             o[nn][dt] = M::mma(va, __builtin_bit_cast(bf16x8_t, pt.v[mp][nn]), o[nn][dt]);
+          if (dt == S::DT - 1) {
+            const bf16x8_t ones = __builtin_bit_cast(
+                bf16x8_t, u32x4{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair});
+#pragma unroll
+            for (int nn = 0; nn < kRowTiles; ++nn)
+              osum[nn] = M::mma(ones, __builtin_bit_cast(bf16x8_t, pt.v[mp][nn]), osum[nn]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -952,7 +968,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int work, uin
   // ---- write rows: lane holds dims 16dt + 4g .. +3 of row l16 ----
   float l_row[kRowTiles];
 #pragma unroll
-  for (int n = 0; n < kRowTiles; ++n) l_row[n] = rows_sum(l_run[n]);   // whole wave, before any exit
+  for (int n = 0; n < kRowTiles; ++n)
+    l_row[n] = TWO ? osum[n][0] : rows_sum(l_run[n]);   // whole wave, before any exit
 #pragma unroll
   for (int n = 0; n < kRowTiles; ++n) {
     if (!row_ok[n]) continue;
